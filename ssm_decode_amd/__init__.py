@@ -1,0 +1,13 @@
+"""ReplaySSM decode path for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+include/replayssm.h (libreplayssm.so, built by `python -m ssm_decode_amd.build`).
+This package only marshals torch tensors into those calls; see _lib.py.
+"""
+from ._lib import (  # noqa: F401
+    BF16_SHARED, DEVERR_ACCEPT, DEVERR_APPEND_OVERFLOW, DEVERR_CORRUPT, DEVERR_PENDING, EHIP, EINVAL,
+    ENOTSUP, FP32, FP32_HP_BF16_LP, GDN, MAMBA2, OK, Config, LayerState, ReplaySSMError, SIGNATURES,
+    STRING_FUNCTIONS, LIB_PATH, State, Sizes, accept, append, decode, eager_accept, eager_step,
+    eager_verify, flush, get_sizes, init, last_error, lib, make_config, pack_state, read_error,
+    status_string, unpack_state, verify,
+)

@@ -1,0 +1,126 @@
+// Internal declarations shared by the HIP sources of libreplayssm (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "replayssm.h"
+
+namespace rs {
+
+// ---------------------------------------------------------------------------
+// Checkpoint layout on the device (private to the library).
+//
+// A head's dv x dk fp32 state is cut into 16 x 16 tiles; tile (pt, nt) covers
+// rows p = 16 pt .. 16 pt + 15 and columns n = 16 nt .. 16 nt + 15 and is stored
+// as 1 KiB at float offset (pt * NT + nt) * 256, NT = dk / 16. Inside a tile,
+// lane l (0..63) of a wavefront owns one float4:
+//     row p = 16 pt + (l & 15), columns n = 16 nt + 4 (l >> 4) + {0, 1, 2, 3}
+// This is exactly the accumulator layout of v_mfma_f32_16x16x4_f32 when the
+// MFMA's M index runs over n and its N index over p, so a fold can seed the
+// accumulators with one 16-byte load per lane and store them back the same
+// way, and a wavefront's load of one tile is one contiguous 1 KiB.
+//
+// The bf16 copy pairs tiles (pt, 2m) and (pt, 2m + 1) into one 1 KiB chunk at
+// bf16 offset (pt * NT/2 + m) * 512; lane l owns 8 bf16 (16 bytes): elements
+// 0..3 are its float4 of tile 2m, elements 4..7 its float4 of tile 2m + 1.
+// ---------------------------------------------------------------------------
+constexpr int kWave = 64;
+constexpr int kMaxDrafts = 8;
+constexpr int kMaxL = 64;
+constexpr int kMaxDv = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Mode : int { kModeDecode = 0, kModeVerify = 1, kModeFlush = 2 };
+
+struct ReplayArgs {
+  float* hp;
+  uint16_t* lp;
+  const float* ring_alpha;
+  const float* ring_beta;
+  const float* ring_k;
+  float* ring_v;
+  int32_t* head;
+  int32_t* h;
+  int32_t* p;
+  int64_t* folded;
+  int32_t* arrive;
+  int32_t* err;
+  const float* q;  // [B][T][H][dk]
+  float* out;      // [B][T][H][dv]
+  int B, H, dv, L, C, T;
+  int precision;
+  int mode;
+};
+
+struct AppendArgs {
+  float* ring_alpha;
+  float* ring_beta;
+  float* ring_k;
+  float* ring_v;
+  int32_t* head;
+  int32_t* h;
+  int32_t* p;
+  int32_t* arrive;
+  int32_t* err;
+  const float* alpha;
+  const float* beta;
+  const float* k;
+  const float* v;
+  int B, H, dv, dk, C, T, T_max;
+  int units_per_seq;  // float4 units of k and v per sequence
+};
+
+struct EagerArgs {
+  float* S;             // [B][H][slots][dv*dk] private layout
+  const int32_t* slot;  // [B] or NULL (in-place step)
+  const float* alpha;   // [B][T][H]
+  const float* beta;
+  const float* k;  // [B][T][H][dk]
+  const float* v;  // [B][T][H][dv]
+  const float* q;  // [B][T][H][dk]
+  float* out;      // [B][T][H][dv]
+  int B, H, dv, T, nslots;
+};
+
+// Dynamic LDS carve-up of the replay kernel, in floats. Every block starts on a
+// 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
+// wavefront reading one column of four consecutive rows hit distinct banks.
+struct ReplayLds {
+  int dks, dvs;  // row strides of the k and v record rows
+  int k, v, alpha, beta, q, gq, gk, cq, ck, gf, total;
+  __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
+  __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
+    dks = row_stride(dk);
+    dvs = row_stride(dv);
+    k = 0;
+    v = k + C * dks;
+    alpha = v + C * dvs;
+    beta = alpha + pad4(C);
+    q = beta + pad4(tmax);
+    gq = q + tmax * dk;
+    gk = gq + pad4((C + 1) * tmax);
+    cq = gk + pad4((C + 1) * tmax);
+    ck = cq + pad4(C * tmax);
+    gf = ck + pad4(C * tmax);
+    total = gf + pad4(C + 1);
+  }
+};
+
+// Launchers (one per kernel family); they return hipError_t of the launch.
+hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStream_t s);
+hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s);
+hipError_t launch_accept(int32_t* h, int32_t* p, int32_t* err, const int32_t* acc, int B, int L,
+                         hipStream_t s);
+hipError_t launch_init(int32_t* head, int32_t* h, int32_t* p, int64_t* folded, int32_t* arrive,
+                       int32_t* err, int B, hipStream_t s);
+hipError_t launch_pack(const float* src, float* hp, uint16_t* lp, int64_t nheads, int dv, int dk,
+                       hipStream_t s);
+hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_t nheads, int dv,
+                         int dk, hipStream_t s);
+hipError_t launch_eager(int kind, int dk, const EagerArgs& a, hipStream_t s);
+hipError_t launch_eager_accept(int32_t* slot, const int32_t* acc, int B, int T, hipStream_t s);
+
+}  // namespace rs

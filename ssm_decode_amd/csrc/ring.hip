@@ -1,0 +1,185 @@
+// Buffer and pointer kernels of libreplayssm: append, accept, init, and the
+// conversions between the logical checkpoint order and the private layouts.
+#include "device.hpp"
+
+namespace rs {
+
+// Append: the T new records of every head of sequence b go to ring slots
+// (head + h + p + i) mod C ("ReplaySSM: Cache SSM Inputs, Not State", How it
+// works: each step appends its inputs; drafts are appended together and the
+// buffer is circular with capacity L + T). Grid (chunks, B): the chunks of a
+// sequence copy its k and v rows as float4 units; the source side is one
+// contiguous span per sequence. The last chunk to finish publishes p += T.
+template <int KIND>
+__global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
+  const int b = blockIdx.y;
+  const int head = a.head[b], hc = a.h[b], pend = a.p[b];
+  const int T = a.T, H = a.H, C = a.C, dk = a.dk, dv = a.dv;
+  const int L = C - a.T_max;
+  const bool corrupt = head < 0 || head >= C || hc < 0 || hc > L || pend < 0;
+  const bool bad = corrupt || pend + T > a.T_max;
+  const int first = head + hc + pend;
+  if (!bad) {
+    const int dk4 = dk >> 2, dv4 = dv >> 2;
+    const int nk = T * H * dk4;
+    const float* ksrc = a.k + (int64_t)b * T * H * dk;
+    const float* vsrc = a.v + (int64_t)b * T * H * dv;
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < a.units_per_seq; u += gridDim.x * 256) {
+      if (u < nk) {
+        const int c4 = u % dk4, th = u / dk4;
+        const int hd = th % H, i = th / H;
+        const int slot = (first + i) % C;
+        st4(a.ring_k + (((int64_t)b * H + hd) * C + slot) * dk + 4 * c4, ld4(ksrc + 4 * (int64_t)u));
+      } else {
+        const int uv = u - nk;
+        const int c4 = uv % dv4, th = uv / dv4;
+        const int hd = th % H, i = th / H;
+        const int slot = (first + i) % C;
+        st4(a.ring_v + (((int64_t)b * H + hd) * C + slot) * dv + 4 * c4, ld4(vsrc + 4 * (int64_t)uv));
+      }
+    }
+    if (blockIdx.x == 0) {
+      for (int u = threadIdx.x; u < T * H; u += 256) {
+        const int hd = u % H, i = u / H;
+        const int slot = (first + i) % C;
+        const int64_t dst = ((int64_t)b * H + hd) * C + slot;
+        const int64_t src = ((int64_t)b * T + i) * H + hd;
+        a.ring_alpha[dst] = a.alpha[src];
+        if (KIND == REPLAYSSM_GDN) a.ring_beta[dst] = a.beta[src];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && arrive_last(a.arrive, b, gridDim.x)) {
+    if (bad)
+      atomicOr(a.err, corrupt ? REPLAYSSM_DEVERR_CORRUPT : REPLAYSSM_DEVERR_APPEND_OVERFLOW);
+    else
+      a.p[b] = pend + T;
+  }
+}
+
+hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s) {
+  const int per_block = 256 * 4;
+  int chunks = (a.units_per_seq + per_block - 1) / per_block;
+  if (chunks < 1) chunks = 1;
+  const dim3 grid((unsigned)chunks, (unsigned)a.B);
+  if (kind == REPLAYSSM_GDN)
+    hipLaunchKernelGGL(append_kernel<REPLAYSSM_GDN>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<REPLAYSSM_MAMBA2>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Accept: the accepted prefix only moves the pointer (h += a, p = 0); rejected
+// records stay where they are until the next append overwrites them ("How it
+// works": Speculative decoding).
+__global__ void __launch_bounds__(256) accept_kernel(int32_t* h, int32_t* p, int32_t* err,
+                                                     const int32_t* acc, int B, int L) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int hb = h[b], pb = p[b];
+  if (hb < 0 || hb > L || pb < 0) {
+    atomicOr(err, REPLAYSSM_DEVERR_CORRUPT);
+    return;
+  }
+  int lim = L - hb < pb ? L - hb : pb;
+  if (lim < 0) lim = 0;
+  int ab = acc[b];
+  if (ab < 0 || ab > lim) {
+    atomicOr(err, REPLAYSSM_DEVERR_ACCEPT);
+    ab = ab < 0 ? 0 : lim;
+  }
+  h[b] = hb + ab;
+  p[b] = 0;
+}
+
+hipError_t launch_accept(int32_t* h, int32_t* p, int32_t* err, const int32_t* acc, int B, int L,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, h, p, err,
+                     acc, B, L);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) init_kernel(int32_t* head, int32_t* h, int32_t* p,
+                                                   int64_t* folded, int32_t* arrive, int32_t* err,
+                                                   int B) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b == 0) *err = 0;
+  if (b >= B) return;
+  head[b] = 0;
+  h[b] = 0;
+  p[b] = 0;
+  folded[b] = 0;
+  arrive[b] = 0;
+}
+
+hipError_t launch_init(int32_t* head, int32_t* h, int32_t* p, int64_t* folded, int32_t* arrive,
+                       int32_t* err, int B, hipStream_t s) {
+  hipLaunchKernelGGL(init_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, head, h, p,
+                     folded, arrive, err, B);
+  return hipGetLastError();
+}
+
+// Logical [heads][dv][dk] fp32 <-> private tile layouts. One thread per
+// (head, tile, lane): four consecutive columns of one row.
+__global__ void __launch_bounds__(256) pack_kernel(const float* src, float* hp, uint16_t* lp,
+                                                   int64_t nheads, int dv, int dk) {
+  const int NT = dk >> 4, PT = dv >> 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= nheads * PT * NT * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t t = gid >> 6;
+  const int tile = (int)(t % (PT * NT));
+  const int64_t hh = t / (PT * NT);
+  const int pt = tile / NT, nt = tile - pt * NT;
+  const int p = 16 * pt + (lane & 15), n = 16 * nt + 4 * (lane >> 4);
+  const int64_t base = hh * (int64_t)dv * dk;
+  const f32x4 x = ld4(src + base + (int64_t)p * dk + n);
+  if (hp) st4(hp + base + tile * 256 + lane * 4, x);
+  if (lp) {
+    uint2* d = reinterpret_cast<uint2*>(lp + base + (pt * (NT / 2) + nt / 2) * 512 + lane * 8 +
+                                        (nt & 1) * 4);
+    *d = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  }
+}
+
+__global__ void __launch_bounds__(256) unpack_kernel(const float* hp, const uint16_t* lp, float* dst,
+                                                     int64_t nheads, int dv, int dk) {
+  const int NT = dk >> 4, PT = dv >> 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= nheads * PT * NT * 64) return;
+  const int lane = (int)(gid & 63);
+  const int64_t t = gid >> 6;
+  const int tile = (int)(t % (PT * NT));
+  const int64_t hh = t / (PT * NT);
+  const int pt = tile / NT, nt = tile - pt * NT;
+  const int p = 16 * pt + (lane & 15), n = 16 * nt + 4 * (lane >> 4);
+  const int64_t base = hh * (int64_t)dv * dk;
+  f32x4 x;
+  if (hp) {
+    x = ld4(hp + base + tile * 256 + lane * 4);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(lp + base + (pt * (NT / 2) + nt / 2) * 512 +
+                                                     lane * 8 + (nt & 1) * 4);
+    x = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  }
+  st4(dst + base + (int64_t)p * dk + n, x);
+}
+
+hipError_t launch_pack(const float* src, float* hp, uint16_t* lp, int64_t nheads, int dv, int dk,
+                       hipStream_t s) {
+  const int64_t threads = nheads * (dv / 16) * (dk / 16) * 64;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, hp,
+                     lp, nheads, dv, dk);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_t nheads, int dv,
+                         int dk, hipStream_t s) {
+  const int64_t threads = nheads * (dv / 16) * (dk / 16) * 64;
+  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, hp,
+                     lp, dst, nheads, dv, dk);
+  return hipGetLastError();
+}
+
+}  // namespace rs

@@ -1,0 +1,116 @@
+"""The C-ABI library: loads, exports every declared symbol, validates on the host.
+
+No call here reaches the GPU: each either only sizes, or fails validation
+before anything would be enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "replayssm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int)\s+(replayssm_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def rs():
+    import ssm_decode_amd
+
+    ssm_decode_amd.lib()
+    return ssm_decode_amd
+
+
+def test_header_declares_the_five_path_calls():
+    names = declared_functions()
+    for n in ("replayssm_append", "replayssm_decode", "replayssm_verify", "replayssm_flush", "replayssm_accept"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(rs):
+    out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (replayssm_\w+)", out))
+    missing = set(declared_functions()) - exported
+    assert not missing, missing
+    # and the binding wraps every one of them
+    assert set(declared_functions()) == set(rs.SIGNATURES) | set(rs.STRING_FUNCTIONS)
+
+
+def test_library_has_no_oracle_dependency(rs):
+    out = subprocess.run(["nm", "-D", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "oracle_" not in out
+    ldd = subprocess.run(["readelf", "-d", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "liboracle" not in ldd
+
+
+def test_sizes_of_the_b256_mamba2_layer(rs):
+    s = rs.get_sizes(rs.make_config("mamba2", "fp32", 256, 128, 64, 128, 16, 1))
+    assert s.C == 17
+    assert s.hp_bytes == 256 * 128 * 64 * 128 * 4 == 1 << 30
+    assert s.lp_bytes == 0
+    assert s.ring_k_bytes == 256 * 128 * 17 * 128 * 4
+    assert s.ring_v_bytes == 256 * 128 * 17 * 64 * 4
+    s2 = rs.get_sizes(rs.make_config("mamba2", "fp32_hp_bf16_lp", 256, 128, 64, 128, 16, 4))
+    assert s2.C == 20 and s2.lp_bytes == s2.hp_bytes // 2
+    s3 = rs.get_sizes(rs.make_config("mamba2", "bf16_shared", 2, 2, 64, 128, 16, 4))
+    assert s3.hp_bytes == 0 and s3.lp_bytes > 0
+    s4 = rs.get_sizes(rs.make_config("gdn", "fp32", 256, 32, 128, 128, 16, 4))
+    assert s4.ring_beta_bytes == 256 * 32 * 20 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=5), -1), (dict(precision=7), -1), (dict(B=0), -1), (dict(B=70000), -1), (dict(H=0), -1),
+    (dict(dv=24), -1), (dict(dv=272), -1), (dict(dk=48), -1), (dict(dk=256), -1), (dict(L=0), -1),
+    (dict(L=65), -1), (dict(T_max=0), -1), (dict(T_max=9, L=16), -1), (dict(T_max=5, L=4), -1),
+    (dict(precision="fp32_hp_bf16_lp", dk=16, dv=16), -2), (dict(kind="gdn", precision="bf16_shared"), -2),
+    (dict(L=64, T_max=8, dv=256, dk=128), -2),
+])
+def test_config_validation(rs, kw, code):
+    base = dict(kind="mamba2", precision="fp32", B=2, H=3, dv=64, dk=128, L=16, T_max=4)
+    base.update(kw)
+    cfg = rs.make_config(**base)
+    sz = rs.Sizes()
+    assert rs.lib().replayssm_get_sizes(ctypes.byref(cfg), ctypes.byref(sz)) == code
+    assert rs.last_error()
+
+
+def test_calls_reject_bad_arguments_before_enqueueing(rs):
+    L = rs.lib()
+    cfg = rs.make_config("mamba2", "fp32", 2, 3, 64, 128, 16, 4)
+    st = rs.State()  # all NULL
+    assert L.replayssm_init(ctypes.byref(cfg), ctypes.byref(st), None) == rs.EINVAL
+    assert L.replayssm_init(ctypes.byref(cfg), None, None) == rs.EINVAL
+    assert L.replayssm_decode(None, ctypes.byref(st), None, None, None) == rs.EINVAL
+    fake = 1 << 20  # aligned, never dereferenced: validation fails first
+    st_ok = rs.State(*([fake] * 12))
+    st_ok.lp = None
+    st_ok.ring_beta = None
+    assert L.replayssm_append(ctypes.byref(cfg), ctypes.byref(st_ok), 0, fake, fake, fake, None, None) == rs.EINVAL
+    assert L.replayssm_append(ctypes.byref(cfg), ctypes.byref(st_ok), 5, fake, fake, fake, None, None) == rs.EINVAL
+    assert "T=5" in rs.last_error()
+    assert L.replayssm_verify(ctypes.byref(cfg), ctypes.byref(st_ok), 9, fake, fake, None) == rs.EINVAL
+    assert L.replayssm_decode(ctypes.byref(cfg), ctypes.byref(st_ok), fake + 4, fake, None) == rs.EINVAL
+    assert "aligned" in rs.last_error()
+    assert L.replayssm_accept(ctypes.byref(cfg), ctypes.byref(st_ok), None, None) == rs.EINVAL
+    cfg_lp = rs.make_config("mamba2", "fp32_hp_bf16_lp", 2, 3, 64, 128, 16, 4)
+    assert L.replayssm_flush(ctypes.byref(cfg_lp), ctypes.byref(st_ok), None) == rs.EINVAL  # lp missing
+    assert L.replayssm_eager_step(ctypes.byref(cfg_lp), fake, fake, fake, fake, None, fake, fake, None) == rs.EINVAL
+    cfg_g = rs.make_config("gdn", "fp32", 2, 3, 64, 128, 16, 4)
+    assert L.replayssm_eager_step(ctypes.byref(cfg_g), fake, fake, fake, fake, None, fake, fake, None) == rs.EINVAL
+    assert L.replayssm_eager_accept(ctypes.byref(cfg), fake, fake, 0, None) == rs.EINVAL
+    assert L.replayssm_pack_state(ctypes.byref(cfg), fake, None, None, None) == rs.EINVAL
+    assert L.replayssm_unpack_state(ctypes.byref(cfg), None, None, fake, None) == rs.EINVAL
+    assert L.replayssm_read_error(None, None, None) == rs.EINVAL
+
+
+def test_status_strings(rs):
+    assert rs.status_string(0) == "ok"
+    assert rs.status_string(-1) == "invalid argument"
+    assert rs.status_string(-2) == "not supported"
+    assert rs.status_string(-3) == "HIP runtime error"

@@ -1,0 +1,100 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: outputs within max relative error 1e-4 (fp32 checkpoint); the checkpoint
+after folds within 1e-4 of the oracle's state at position `folded`; pointer
+arrays and ring copies bit-exact; no device error bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ssm_decode_amd as rs
+from synth import LayerShape, WORKLOADS
+
+from harness import Runner, run_spec, run_standard, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _assert_clean(rep, tol=TOL, tol_ckpt=TOL):
+    assert rep.pointer_mismatch == 0, (rep.final_pointers, rep.oracle_pointers)
+    assert rep.ring_mismatch == 0
+    assert rep.err_word == 0
+    assert rep.max_rel <= tol, rep.max_rel
+    assert rep.max_rel_ckpt <= tol_ckpt, rep.max_rel_ckpt
+    assert rep.max_rel_u <= tol, rep.max_rel_u
+
+
+def test_tiny_workload_every_output():
+    """B=1, H=2, P=N=16, L=4: 64 decode steps, every output, 15 folds."""
+    w = WORKLOADS["mamba2_tiny"]
+    r = Runner(w.shape, w.L, w.T, wid=w.wid, s0_sigma=w.s0_sigma)
+    rep = run_standard(r, w.steps)
+    _assert_clean(rep)
+    assert rep.final_pointers == {"head": [0], "h": [4], "p": [0], "folded": [60]}
+    assert rep.folds == 15
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 32), (64, 64), (64, 128), (128, 128), (48, 64), (256, 32)])
+@pytest.mark.parametrize("L", [1, 3, 16])
+def test_mamba2_shapes_standard(P, N, L):
+    sh = LayerShape("mamba2", 3, 5, P, N)  # 15 heads: no multiple of anything
+    r = Runner(sh, L, 1, wid=10 + L)
+    rep = run_standard(r, 2 * L + 5)
+    _assert_clean(rep)
+
+
+@pytest.mark.parametrize("decay", ["recipe", "slow"])
+def test_mamba2_long_run_slow_decay(decay):
+    """Slow decay (alpha in [0.9, 1)) keeps the checkpoint visible in every output."""
+    sh = LayerShape("mamba2", 2, 3, 64, 128)
+    r = Runner(sh, 16, 1, wid=21, decay=decay)
+    rep = run_standard(r, 120)
+    _assert_clean(rep)
+    assert rep.folds == 2 * 7
+
+
+@pytest.mark.parametrize("P,N", [(128, 128), (32, 64), (16, 16)])
+@pytest.mark.parametrize("decay", ["recipe", "slow"])
+def test_gdn_standard(P, N, decay):
+    sh = LayerShape("gdn", 2, 3, P, N)
+    r = Runner(sh, 4, 1, wid=30, decay=decay)
+    rep = run_standard(r, 23)
+    _assert_clean(rep)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("T,L", [(1, 4), (2, 5), (3, 8), (4, 16), (8, 8), (5, 13)])
+def test_spec_rounds(kind, T, L):
+    """Random accepted prefixes (0..T) including rejected drafts that get overwritten."""
+    sh = LayerShape(kind, 4, 3, 64, 128)
+    r = Runner(sh, L, T, wid=40 + T)
+    rep = run_spec(r, T, 30)
+    _assert_clean(rep)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_explicit_flush_mid_run(kind):
+    sh = LayerShape(kind, 3, 2, 64, 64)
+    r = Runner(sh, 8, 4, wid=50, decay="slow")
+    sh = r.shape
+    for rnd in range(6):
+        x = r.inputs(4)
+        r.append(x, 4)
+        r.verify(x, 4)
+        r.accept(torch.tensor([rnd % 5, 4, 2][: sh.B], dtype=torch.int32, device="cuda"))
+    x = r.inputs(3)
+    r.append(x, 3)  # pending drafts survive the flush
+    r.flush()
+    assert r.check_pointers()
+    assert r.check_checkpoint() <= TOL
+    r.verify(x, 3)
+    r.accept(torch.full((sh.B,), 3, dtype=torch.int32, device="cuda"))
+    r.flush()
+    r.flush()  # second flush is a no-op
+    assert r.check_pointers()
+    assert r.check_checkpoint() <= TOL
+    assert r.error_word() == 0
+    assert r.report.max_rel <= TOL and r.report.max_rel_u <= TOL
