@@ -1,0 +1,410 @@
+"""Benchmark of the ReplaySSM decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick] [--sweep]
+
+A step of the headline workload is one standard decoding step of a Mamba-2 SSM
+layer at B=256, H=128, P=64, N=128 (4 MiB fp32 state per sequence), L=16:
+replayssm_append of the new token's record followed by replayssm_decode (which
+folds the window into the checkpoint every 16th step). Inputs are seeded
+synthetic tensors generated on the GPU before the timed region (a pool of
+distinct steps, cycled when K + W exceeds it). Prints one JSON line:
+
+  value      tokens/s of the whole step (B tokens per step), HIP-event timed over
+             K steps after W warm-up steps, inputs already resident in HBM
+  roofline   the decode kernel (the dominant one): algorithmic bytes per launch
+             (checkpoint read, h+1 records, q, output, checkpoint write on fold
+             steps) / its average launch duration, both measured live in a second
+             pass with events around each launch, against 8 TB/s
+  eager      the conventional kernel that loads and stores the state every step
+  workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint
+  cpu_baseline  the CPU oracle (fp64 eager recurrence, OpenMP over heads) on a
+             bounded sample of the same workload, scaled to tokens/s
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSM-layer decode tokens/sec at B=256 (+ achieved HBM GB/s vs MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES_MAX = 8 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="mamba2_decode_b256")
+    ap.add_argument("--quick", action="store_true", help="headline workload only (no extras, no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# byte model (algorithmic bytes: what the method must move, per head)
+# ----------------------------------------------------------------------------
+
+def record_bytes(kind, P, N):
+    return 4 + 4 * N + 4 * P + (4 if kind == "gdn" else 0)
+
+
+def ckpt_read_bytes(precision, P, N, fold):
+    if precision == "fp32" or (precision == "fp32_hp_bf16_lp" and fold):
+        return 4 * P * N
+    return 2 * P * N
+
+
+def ckpt_write_bytes(precision, P, N):
+    return {"fp32": 4 * P * N, "fp32_hp_bf16_lp": 6 * P * N, "bf16_shared": 2 * P * N}[precision]
+
+
+def replay_launch_bytes(kind, precision, P, N, h, T, fold):
+    """Bytes one head moves in one decode/verify launch with h committed records before it."""
+    b = ckpt_read_bytes(precision, P, N, fold)
+    b += (h + T) * record_bytes(kind, P, N)  # committed records and the drafts' own records
+    b += T * 4 * N + T * 4 * P  # q in, o out
+    if kind == "gdn":
+        b += T * 4 * P  # u written back into the ring
+    if fold:
+        b += ckpt_write_bytes(precision, P, N)
+    return b
+
+
+def append_bytes(kind, P, N, T):
+    return 2 * T * record_bytes(kind, P, N)  # read the inputs, write the ring
+
+
+def eager_bytes(kind, P, N, T, snapshots):
+    # load the state once, store it after every draft (snapshots) or once, plus inputs and outputs
+    stores = T if snapshots else 1
+    per_tok = 4 + 4 * N + 4 * P + 4 * N + 4 * P + (4 if kind == "gdn" else 0)  # alpha,k,v,q,out(,beta)
+    return 4 * P * N * (1 + stores) + T * per_tok
+
+
+# ----------------------------------------------------------------------------
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.e0 = self.torch.cuda.Event(enable_timing=True)
+        self.e1 = self.torch.cuda.Event(enable_timing=True)
+        self.e0.record()
+        return self
+
+    def __exit__(self, *a):
+        self.e1.record()
+        self.torch.cuda.synchronize()
+        self.ms = self.e0.elapsed_time(self.e1)
+
+
+def make_pool(torch, synth, shape, T, n_needed, seed, wid, bytes_per_set):
+    n = int(max(1, min(n_needed, POOL_BYTES_MAX // max(bytes_per_set, 1))))
+    return [synth.device_step(seed, wid, 1000 + i, shape, T, "cuda") for i in range(n)]
+
+
+def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True):
+    """Append + decode steps of a standard-decoding workload; returns timing and byte counts."""
+    sh = w.shape
+    cfg = rs.make_config(sh.kind, w.precision, sh.B, sh.H, sh.P, sh.N, w.L, 1)
+    layer = rs.LayerState(cfg)
+    layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
+    rb = record_bytes(sh.kind, sh.P, sh.N)
+    pool = make_pool(torch, synth, sh, 1, steps + warmup, seed, w.wid, sh.B * sh.H * (rb + 4 * (sh.N + sh.P)))
+    out = torch.empty((sh.B, sh.H, sh.P), dtype=torch.float32, device="cuda")
+    st, stream = layer.struct, torch.cuda.current_stream()
+
+    def step(i):
+        x = pool[i % len(pool)]
+        rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+        rs.decode(cfg, st, x["q"], out, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    h0 = int(layer.h[0].item())
+    with Timer(torch) as tm:
+        for i in range(steps):
+            step(warmup + i)
+    # exact byte count of the timed steps from the pointer rule (all sequences move in step)
+    h, kbytes, nfold = h0, 0, 0
+    for _ in range(steps):
+        fold = h + 1 > w.L
+        kbytes += replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold)
+        nfold += fold
+        h = 1 if fold else h + 1
+    res = {"ms": tm.ms, "steps": steps, "tokens": sh.B * steps, "decode_bytes": kbytes * sh.B * sh.H,
+           "append_bytes": append_bytes(sh.kind, sh.P, sh.N, 1) * sh.B * sh.H * steps, "folds": nfold}
+    if kernel_pass:
+        # second pass: events around every decode launch (same stream as the kernels)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        h1 = int(layer.h[0].item())
+        for i in range(steps):
+            x = pool[(warmup + steps + i) % len(pool)]
+            rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+            evs[i][0].record(stream)
+            rs.decode(cfg, st, x["q"], out, stream)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        durs = np.array([a.elapsed_time(b) for a, b in evs])
+        h, kb, fold_ms, plain_ms, fold_b, plain_b = h1, 0, [], [], 0, 0
+        for i in range(steps):
+            fold = h + 1 > w.L
+            bb = replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold) * sh.B * sh.H
+            kb += bb
+            (fold_ms if fold else plain_ms).append(durs[i])
+            if fold:
+                fold_b += bb
+            else:
+                plain_b += bb
+            h = 1 if fold else h + 1
+        res.update({"kernel_ms_total": float(durs.sum()), "kernel_launches": steps, "kernel_bytes": kb,
+                    "kernel_avg_us": float(durs.mean() * 1e3),
+                    "fold_avg_us": float(np.mean(fold_ms) * 1e3) if fold_ms else None,
+                    "plain_avg_us": float(np.mean(plain_ms) * 1e3) if plain_ms else None,
+                    "fold_gbs": fold_b / (np.sum(fold_ms) * 1e6) if fold_ms else None,
+                    "plain_gbs": plain_b / (np.sum(plain_ms) * 1e6) if plain_ms else None})
+    err = rs.read_error(st)
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    del layer, pool
+    return res
+
+
+def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, kernel_pass=True):
+    sh = w.shape
+    if B is not None:
+        sh = synth.LayerShape(sh.kind, B, sh.H, sh.P, sh.N)
+    prec = precision or w.precision
+    T = w.T if w.T > 1 else int(w.extra.get("spec_T", 4))
+    cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, T)
+    layer = rs.LayerState(cfg)
+    layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
+    rb = record_bytes(sh.kind, sh.P, sh.N)
+    n = warmup + 2 * rounds  # both timed passes get their own acceptance draws
+    pool = make_pool(torch, synth, sh, T, n, seed, w.wid, sh.B * sh.H * T * (rb + 4 * (sh.N + sh.P)))
+    accs = [synth.device_accept(seed, w.wid, r, sh.B, T, "cuda") for r in range(n)]
+    acc_host = [a.cpu().numpy() for a in accs]
+    out = torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda")
+    st, stream = layer.struct, torch.cuda.current_stream()
+
+    def rnd(i, evs=None):
+        x = pool[i % len(pool)]
+        rs.append(cfg, st, T, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+        if evs is not None:
+            evs[0].record(stream)
+        rs.verify(cfg, st, T, x["q"], out, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        rs.accept(cfg, st, accs[i], stream)
+
+    for i in range(warmup):
+        rnd(i)
+    torch.cuda.synchronize()
+    hs = layer.h.cpu().numpy().astype(np.int64)
+    with Timer(torch) as tm:
+        for i in range(rounds):
+            rnd(warmup + i)
+    accepted = int(sum(acc_host[warmup + i].sum() for i in range(rounds)))
+    # per-sequence byte count from the pointer rule
+    kb = 0
+    h = hs.copy()
+    for i in range(rounds):
+        fold = h + T > w.L
+        for f in (False, True):
+            m = fold == f
+            if m.any():
+                kb += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f) for hh in h[m]) * sh.H
+        h = np.where(fold, 0, h) + acc_host[warmup + i]
+    res = {"ms": tm.ms, "rounds": rounds, "accepted_tokens": accepted, "drafts": sh.B * T * rounds,
+           "verify_bytes": int(kb)}
+    if kernel_pass:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+        h = layer.h.cpu().numpy().astype(np.int64)
+        torch.cuda.synchronize()
+        base = warmup + rounds
+        for i in range(rounds):
+            rnd(base + i, evs[i])
+        torch.cuda.synchronize()
+        durs = np.array([a.elapsed_time(b) for a, b in evs])
+        kb2 = 0
+        for i in range(rounds):
+            fold = h + T > w.L
+            for f in (False, True):
+                m = fold == f
+                if m.any():
+                    kb2 += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f) for hh in h[m]) * sh.H
+            h = np.where(fold, 0, h) + acc_host[base + i]
+        res.update({"kernel_avg_us": float(durs.mean() * 1e3), "kernel_gbs": kb2 / (durs.sum() * 1e6)})
+    err = rs.read_error(st)
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    return res
+
+
+def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
+    sh = w.shape
+    cfg = rs.make_config(sh.kind, "fp32", sh.B, sh.H, sh.P, sh.N, w.L, T)
+    nslots = 1 if T == 1 else T + 1
+    S = torch.empty((sh.B, sh.H, nslots, sh.P * sh.N), dtype=torch.float32, device="cuda")
+    S0 = synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda")
+    packed = torch.empty((sh.B, sh.H, sh.P * sh.N), dtype=torch.float32, device="cuda")
+    rs.pack_state(cfg, S0, packed, None)
+    S[:, :, 0].copy_(packed)
+    del S0, packed
+    rb = record_bytes(sh.kind, sh.P, sh.N)
+    pool = make_pool(torch, synth, sh, T, steps + warmup, seed, w.wid, sh.B * sh.H * T * (rb + 4 * (sh.N + sh.P)))
+    out = torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda")
+    slot = torch.zeros(sh.B, dtype=torch.int32, device="cuda")
+    acc = torch.full((sh.B,), T, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x = pool[i % len(pool)]
+        if T == 1:
+            rs.eager_step(cfg, S, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
+        else:
+            rs.eager_verify(cfg, S, slot, T, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
+            rs.eager_accept(cfg, slot, acc, T, stream)
+
+    for i in range(warmup):
+        step(i)
+    with Timer(torch) as tm:
+        for i in range(steps):
+            step(warmup + i)
+    b = eager_bytes(sh.kind, sh.P, sh.N, T, T > 1) * sh.B * sh.H * steps
+    return {"ms": tm.ms, "steps": steps, "tokens": sh.B * T * steps, "bytes": b, "gbs": b / (tm.ms * 1e6)}
+
+
+def cpu_baseline(synth, w, seed, seconds):
+    """The oracle as it stands, on a bounded sample of the workload: B' sequences (all heads)."""
+    import oracle
+
+    sh = w.shape
+    Bs = 64
+    sub = synth.LayerShape(sh.kind, Bs, sh.H, sh.P, sh.N)
+    nh = Bs * sh.H
+    S = synth.host_initial_state(seed, w.wid, sub, w.s0_sigma).reshape(nh, sh.P, sh.N).astype(np.float64)
+    acc = np.ones(nh, np.int32)
+    # a few distinct steps of inputs, reused cyclically (the oracle's work does not depend on values)
+    inputs = []
+    for t in range(4):
+        x = synth.host_step(seed, w.wid, t, sub, 1)
+        inputs.append({k: np.ascontiguousarray(np.swapaxes(v, 1, 2)).reshape(nh, 1, *v.shape[3:])
+                       for k, v in x.items()})
+    steps, spent = 0, 0.0
+    while spent < seconds and steps < 512:
+        args = inputs[steps % len(inputs)]
+        t0 = time.perf_counter()
+        if sh.kind == "mamba2":
+            oracle.mamba2_round(S, args["alpha"].reshape(nh, 1), args["k"], args["v"], args["q"], acc)
+        else:
+            oracle.gdn_round(S, args["alpha"].reshape(nh, 1), args["beta"].reshape(nh, 1), args["k"], args["v"],
+                             args["q"], acc)
+        spent += time.perf_counter() - t0
+        steps += 1
+    return {"value": Bs * steps / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{Bs} of {sh.B} sequences (all {sh.H} heads), {steps} decode steps, fp64 eager "
+                      f"recurrence, {spent:.1f} s of oracle time (input generation excluded)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path has no cross-GPU step (sequences and heads shard "
+              "with no exchange), and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import ssm_decode_amd as rs
+    import synth
+
+    rs.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    sh = w.shape
+    main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed)
+    tok_s = main_res["tokens"] / (main_res["ms"] * 1e-3)
+    achieved = main_res["kernel_bytes"] / (main_res["kernel_ms_total"] * 1e6)
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms"] / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "kind": sh.kind, "B": sh.B, "H": sh.H, "P": sh.P, "N": sh.N, "L": w.L,
+                   "T": 1, "precision": w.precision, "state_MiB_per_seq": sh.H * sh.P * sh.N * 4 / 2**20},
+        "roofline": {"bound": "hbm", "kernel": "replay_kernel (decode)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": main_res["kernel_avg_us"],
+                     "algorithmic_bytes_per_launch": main_res["kernel_bytes"] / main_res["kernel_launches"],
+                     "plain_step_us": main_res["plain_avg_us"], "fold_step_us": main_res["fold_avg_us"],
+                     "plain_step_gbs": main_res["plain_gbs"], "fold_step_gbs": main_res["fold_gbs"]},
+        "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
+    }
+    if not args.quick:
+        eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
+        line["eager"] = {"tokens_per_s": eg["tokens"] / (eg["ms"] * 1e-3), "gbs": eg["gbs"],
+                         "frac": eg["gbs"] / HBM_PEAK_GBS,
+                         "speedup_of_replay": tok_s / (eg["tokens"] / (eg["ms"] * 1e-3)),
+                         "state_bytes_per_step_eager": 2 * 4 * sh.P * sh.N,
+                         "state_bytes_per_step_replay": 4 * sh.P * sh.N * (1 + 1.0 / w.L)}
+        wl = {}
+        w2 = synth.WORKLOADS["mamba2_spec_b256"]
+        r2 = run_spec(torch, rs, synth, w2, 128, 8, args.seed)
+        e2 = run_eager(torch, rs, synth, w2, 64, 4, args.seed, T=w2.T)
+        wl[w2.name] = {"accepted_tokens_per_s": r2["accepted_tokens"] / (r2["ms"] * 1e-3),
+                       "drafts_per_s": r2["drafts"] / (r2["ms"] * 1e-3),
+                       "verify_kernel_gbs": r2["kernel_gbs"], "verify_avg_us": r2["kernel_avg_us"],
+                       "eager_snapshot_drafts_per_s": e2["tokens"] / (e2["ms"] * 1e-3), "eager_snapshot_gbs": e2["gbs"]}
+        w3 = synth.WORKLOADS["gdn_decode_b256"]
+        r3 = run_standard_decode(torch, rs, synth, w3, 256, 16, args.seed)
+        e3 = run_eager(torch, rs, synth, w3, 256, 16, args.seed)
+        r3s = run_spec(torch, rs, synth, w3, 64, 8, args.seed)
+        wl[w3.name] = {"tokens_per_s": r3["tokens"] / (r3["ms"] * 1e-3),
+                       "decode_kernel_gbs": r3["kernel_bytes"] / (r3["kernel_ms_total"] * 1e6),
+                       "eager_tokens_per_s": e3["tokens"] / (e3["ms"] * 1e-3), "eager_gbs": e3["gbs"],
+                       "verify_T4_accepted_tokens_per_s": r3s["accepted_tokens"] / (r3s["ms"] * 1e-3),
+                       "verify_T4_kernel_gbs": r3s["kernel_gbs"]}
+        w4 = synth.WORKLOADS["mamba2_2prec_b256"]
+        r4 = {}
+        for prec in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):
+            r = run_spec(torch, rs, synth, w4, 128, 8, args.seed, precision=prec)
+            r4[prec] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
+                        "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"]}
+        if args.sweep:
+            for B in (1, 32, 512):
+                r = run_spec(torch, rs, synth, w4, 64, 8, args.seed, B=B)
+                r4[f"fp32_hp_bf16_lp_B{B}"] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
+                                               "verify_kernel_gbs": r["kernel_gbs"]}
+        wl[w4.name] = r4
+        line["workloads"] = wl
+    if not (args.quick or args.no_cpu_baseline):
+        line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

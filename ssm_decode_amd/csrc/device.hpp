@@ -58,12 +58,19 @@ __device__ __forceinline__ float sum_width(float x) {
 // other workgroup of b read them before arriving, so nothing reads them after.
 // The caller must have synchronised its workgroup before calling. The counter
 // is reset to zero for the next launch.
+//
+// No fence is needed, and none is issued: nothing is published through the
+// counter. A workgroup's pointer reads have returned before its relaxed
+// agent-scope atomic is issued (every address and branch of the workgroup
+// depends on them), and the last workgroup writes the pointers only after its
+// own atomic has returned, i.e. after every other arrival. The new pointer
+// values become visible to the next kernel at the kernel boundary. (An
+// agent-scope fence here would write back and invalidate the XCD's L2 once
+// per workgroup, which costs more than the whole decode.)
 __device__ __forceinline__ bool arrive_last(int32_t* arrive, int b, int expected) {
-  __threadfence();
   const int prev = atomicAdd(arrive + b, 1);
   if (prev != expected - 1) return false;
-  __threadfence();
-  arrive[b] = 0;
+  atomicExch(arrive + b, 0);
   return true;
 }
 
