@@ -173,6 +173,12 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
             else:
                 plain_b += bb
             h = 1 if fold else h + 1
+        by_h = {}
+        hh = h1
+        for i in range(steps):
+            by_h.setdefault(hh, []).append(durs[i] * 1e3)
+            hh = 1 if hh + 1 > w.L else hh + 1
+        res["us_by_h"] = {int(k): round(float(np.mean(v)), 1) for k, v in sorted(by_h.items())}
         res.update({"kernel_ms_total": float(durs.sum()), "kernel_launches": steps, "kernel_bytes": kb,
                     "kernel_avg_us": float(durs.mean() * 1e3),
                     "fold_avg_us": float(np.mean(fold_ms) * 1e3) if fold_ms else None,
@@ -361,7 +367,8 @@ def main():
                      "avg_launch_us": main_res["kernel_avg_us"],
                      "algorithmic_bytes_per_launch": main_res["kernel_bytes"] / main_res["kernel_launches"],
                      "plain_step_us": main_res["plain_avg_us"], "fold_step_us": main_res["fold_avg_us"],
-                     "plain_step_gbs": main_res["plain_gbs"], "fold_step_gbs": main_res["fold_gbs"]},
+                     "plain_step_gbs": main_res["plain_gbs"], "fold_step_gbs": main_res["fold_gbs"],
+                     "us_by_h_before_step": main_res["us_by_h"]},
         "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
     }
     if not args.quick:

@@ -36,6 +36,9 @@ def common_flags():
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
+        # every atomic of the library is issued by a single lane; the wave-level
+        # aggregation rewrite would only add a wait right after each of them
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     ]
 
 

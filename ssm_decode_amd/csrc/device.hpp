@@ -31,6 +31,60 @@ __device__ __forceinline__ uint4 pack_lp_chunk(const f32x4& a, const f32x4& b) {
                pack_bf16x2(b[2], b[3])};
 }
 
+// Checkpoints are streamed: every byte is read once per call and never again
+// before the next call, so their loads and stores are non-temporal (they do not
+// displace the ring records, which the next kernel reads again, from the caches).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 ld4_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void st4_stream(float* p, const f32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+// A head's fp32 checkpoint (private tile layout) into the registers of one
+// wavefront: tile (wave, nt) is the lane's float4 S[nt].
+template <int NT>
+__device__ __forceinline__ void load_hp(const float* head_base, int wave, int lane, f32x4 (&S)[NT]) {
+  const float* src = head_base + (wave * NT) * 256 + lane * 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) S[nt] = ld4_stream(src + nt * 256);
+}
+
+template <int NT>
+__device__ __forceinline__ void store_hp(float* head_base, int wave, int lane, const f32x4 (&S)[NT]) {
+  float* dst = head_base + (wave * NT) * 256 + lane * 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) st4_stream(dst + nt * 256, S[nt]);
+}
+
+// The same from the bf16 copy (pairs of tiles per 16-byte chunk), widened exactly.
+template <int NT>
+__device__ __forceinline__ void load_lp(const uint16_t* head_base, int wave, int lane, f32x4 (&S)[NT]) {
+  static_assert(NT % 2 == 0, "the bf16 layout pairs tiles");
+  const u32x4* src = reinterpret_cast<const u32x4*>(head_base) + (wave * NT / 2) * 64 + lane;
+#pragma unroll
+  for (int m = 0; m < NT / 2; ++m) {
+    const u32x4 w = __builtin_nontemporal_load(src + m * 64);
+    unpack_lp_chunk(uint4{w[0], w[1], w[2], w[3]}, S[2 * m], S[2 * m + 1]);
+  }
+}
+
+// fp32 registers -> bf16 copy (round to nearest even); returns the rounded values in S when asked.
+template <int NT>
+__device__ __forceinline__ void store_lp(uint16_t* head_base, int wave, int lane, f32x4 (&S)[NT],
+                                         bool keep_rounded) {
+  static_assert(NT % 2 == 0, "the bf16 layout pairs tiles");
+  u32x4* dst = reinterpret_cast<u32x4*>(head_base) + (wave * NT / 2) * 64 + lane;
+#pragma unroll
+  for (int m = 0; m < NT / 2; ++m) {
+    const uint4 x = pack_lp_chunk(S[2 * m], S[2 * m + 1]);
+    __builtin_nontemporal_store(u32x4{x.x, x.y, x.z, x.w}, dst + m * 64);
+    if (keep_rounded) unpack_lp_chunk(x, S[2 * m], S[2 * m + 1]);
+  }
+}
+
 __device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
@@ -53,11 +107,12 @@ __device__ __forceinline__ float sum_width(float x) {
   return x;
 }
 
-// Counts the workgroups of sequence b that have finished; returns true in the
-// single thread of the last one, which may then update b's pointers: every
+// Arrival counting for the per-sequence pointer update ("last arriver").
+// Counts the workgroups of sequence b that have read b's pointers; returns
+// true in the single thread of the last one, which may then update them: every
 // other workgroup of b read them before arriving, so nothing reads them after.
-// The caller must have synchronised its workgroup before calling. The counter
-// is reset to zero for the next launch.
+// The caller must have synchronised its workgroup after its pointer reads. The
+// counter is reset to zero for the next launch.
 //
 // No fence is needed, and none is issued: nothing is published through the
 // counter. A workgroup's pointer reads have returned before its relaxed
@@ -66,7 +121,8 @@ __device__ __forceinline__ float sum_width(float x) {
 // own atomic has returned, i.e. after every other arrival. The new pointer
 // values become visible to the next kernel at the kernel boundary. (An
 // agent-scope fence here would write back and invalidate the XCD's L2 once
-// per workgroup, which costs more than the whole decode.)
+// per workgroup, which costs more than the whole decode.) The replay kernel
+// splits the same protocol in two (atomic early, test late).
 __device__ __forceinline__ bool arrive_last(int32_t* arrive, int b, int expected) {
   const int prev = atomicAdd(arrive + b, 1);
   if (prev != expected - 1) return false;

@@ -32,7 +32,7 @@ __global__ void __launch_bounds__(1024) eager_kernel(const EagerArgs a) {
   if (s0 < 0 || s0 >= ns) s0 = 0;  // never address outside the pool
   f32x4 S[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) S[nt] = ld4(pool + s0 * hsz + nt * 256);
+  for (int nt = 0; nt < NT; ++nt) S[nt] = ld4_stream(pool + s0 * hsz + nt * 256);
 
   for (int i = 0; i < T; ++i) {
     const int64_t tok = ((int64_t)b * T + i) * H + hd;
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(1024) eager_kernel(const EagerArgs a) {
     int sl = s0 + i + 1;
     while (sl >= ns) sl -= ns;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st4(pool + sl * hsz + nt * 256, S[nt]);
+    for (int nt = 0; nt < NT; ++nt) st4_stream(pool + sl * hsz + nt * 256, S[nt]);
   }
 }
 

@@ -29,6 +29,7 @@ constexpr int kWave = 64;
 constexpr int kMaxDrafts = 8;
 constexpr int kMaxL = 64;
 constexpr int kMaxDv = 256;
+constexpr int kStageRegs = 5;  // float4 record units per thread kept in flight at once
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -108,6 +109,11 @@ struct ReplayLds {
     total = gf + pad4(C + 1);
   }
 };
+
+// Grid size for a persistent kernel: as many workgroups as can be resident on
+// the current device at once (occupancy x compute units), at most `items`.
+// The occupancy of each (kernel, block, LDS) triple is computed once and cached.
+hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid);
 
 // Launchers (one per kernel family); they return hipError_t of the launch.
 hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStream_t s);

@@ -1,45 +1,205 @@
 // Replay kernel of libreplayssm: standard decode, output-only draft
 // verification and the checkpoint fold, for Mamba-2 and Gated DeltaNet heads.
 //
-// One workgroup owns one (sequence b, head) pair and one wavefront owns one
-// 16-row tile of the head's state (dv / 16 wavefronts). A call:
+// The work items are (sequence b, head) pairs. A workgroup holds one item at a
+// time, one wavefront per 16-row tile of the head's state (dv / 16
+// wavefronts), and walks its items with the stride of the grid (persistent
+// workgroups). For one item:
 //
-//  1. streams the head's checkpoint from HBM into registers (fp32, or the bf16
-//     copy on non-fold steps in the two-precision mode), and stages the records
-//     of the ring (alpha, k, v / u) plus the drafts' q in LDS;
-//  2. decides the route per sequence: fold when h + T > L (flowchart in
+//  1. its checkpoint sits in registers (fp32, or the bf16 copy on non-fold
+//     steps in the two-precision mode) and its ring records (alpha, k, v / u)
+//     plus the drafts' q go to LDS; both were requested while the workgroup
+//     worked on its previous item;
+//  2. the route is decided per sequence: fold when h + T > L (flowchart in
 //     "ReplaySSM: Cache SSM Inputs, Not State", How it works); the flush call
 //     folds whenever h > 0;
 //  3. fold route: S <- Gamma_h S + V diag(gamma) K^T over the h committed
 //     records as MFMA rank-4 steps whose accumulators are the checkpoint
-//     registers themselves, then writes the fp32 and/or bf16 checkpoint; the
-//     drafts are then replayed on top of the new state held in registers (the
-//     author's reply on the flush route: the state from one V K^T product, the
-//     output by multiplying it with q);
+//     registers themselves, then the fp32 and/or bf16 checkpoint is written;
+//     the drafts are then replayed on top of the new state held in registers
+//     (the author's reply on the flush route: the state from one V K^T
+//     product, the output by multiplying it with q);
 //  4. replay route (no state write): o_i = Gamma_i S q_i
 //     + sum_r gamma_{r,i} (k_r . q_i) v_r over the buffered records r up to
 //     draft i ("How it works": Standard decoding and Speculative decoding);
 //     the k_r . q_i products are wavefront reductions, the decay products
-//     gamma are running products of alpha (no logarithms, so alpha = 0 is
+//     gamma are products of alpha (suffix scans, no logarithms, so alpha = 0 is
 //     exact);
 //  5. GDN: u_i = beta_i (v_i - alpha_i S_{i-1} k_i) with S_{i-1} k_i rebuilt
 //     from S k_i and the buffer ("How it works": Gated DeltaNet), sequential
 //     over the drafts, and stored in place of v_i;
-//  6. the last workgroup of the sequence to finish advances its pointers.
+//  6. the pointers are left alone: the commit kernel, launched right after
+//     this one, advances them (they are read, never written, here).
+//
+// Pipelining: right after step 1 the workgroup requests the next item's ring
+// records (into registers), and as soon as this item's mat-vecs have consumed
+// S, the next item's checkpoint (into S). Both stream in while this item
+// computes. Vector loads complete in order, so the next item can wait for its
+// records without waiting for its checkpoint.
 #include "device.hpp"
+
+#ifndef REPLAYSSM_PREFETCH_DEPTH
+#define REPLAYSSM_PREFETCH_DEPTH 1
+#endif
 
 namespace rs {
 
+// A sequence's buffer pointers as one item reads them.
+struct SeqPtr {
+  int head, h, p;
+};
+
+// What one item does, from its sequence's pointers (the same in every
+// workgroup of the sequence).
+struct Route {
+  int T;        // drafts of this call (0 for flush)
+  bool corrupt; // pointers outside their invariant ranges
+  bool bad;     // corrupt, or a decode/verify call whose pending count is not T
+  bool fold;    // fold the committed records into the checkpoint first
+  bool work;    // anything to do for this item
+  bool outputs; // produce draft outputs
+  int R;        // staged records: committed [0, h), drafts [h, h + T)
+  int r0;       // first record replayed on top of the checkpoint
+};
+
+__device__ __forceinline__ Route route_of(const ReplayArgs& a, const SeqPtr& p) {
+  Route r;
+  r.T = (a.mode == kModeFlush) ? 0 : a.T;
+  r.corrupt = p.head < 0 || p.head >= a.C || p.h < 0 || p.h > a.L || p.p < 0 || p.p > a.C - a.L;
+  r.bad = r.corrupt || ((a.mode != kModeFlush) && (p.p != r.T));
+  r.fold = !r.bad && ((a.mode == kModeFlush) ? (p.h > 0) : (p.h + r.T > a.L));
+  r.work = !r.bad && (a.mode != kModeFlush || r.fold);
+  r.outputs = r.work && (a.mode != kModeFlush);
+  r.R = p.h + r.T;
+  r.r0 = r.fold ? p.h : 0;
+  return r;
+}
+
+// The checkpoint copy a decode/verify call reads for `item` before it knows
+// the route: fp32 in FP32 mode, the bf16 copy otherwise (a fold step of the
+// two-precision mode reloads fp32 once it knows).
+template <int NT>
+__device__ __forceinline__ void load_ckpt_early(const ReplayArgs& a, int item, int wave, int lane,
+                                                f32x4 (&S)[NT]) {
+  const int64_t hoff = (int64_t)item * (a.dv * NT * 16);
+  if (a.precision == REPLAYSSM_FP32) {
+    load_hp<NT>(a.hp + hoff, wave, lane, S);
+  } else if constexpr (NT >= 2) {
+    load_lp<NT>(a.lp + hoff, wave, lane, S);
+  }
+}
+
+// One item's ring rows while they are in flight: up to kRecK k-row and kRecV
+// v-row passes per thread (a pass is nthr / (dk / 4) k rows or 16 v rows), the
+// thread's float4 of the drafts' q, and its alpha / beta.
+constexpr int kRecK = 3, kRecV = 2;
+struct RecRegs {
+  f32x4 kb[kRecK], vb[kRecV], qv;
+  float al, be;
+};
+
+// Where a thread's share of the ring rows lies (k rows: LPR threads per row;
+// v rows: dv / 4 threads per row, 16 rows per pass since nthr = 4 dv).
+struct StageMap {
+  int kstep, rk0, ck, rv0, cv;
+  __device__ __forceinline__ StageMap(int tid, int nthr, int lpr, int dv) {
+    kstep = nthr / lpr;
+    rk0 = tid / lpr;
+    ck = tid % lpr;
+    const int dv4 = dv >> 2;
+    rv0 = tid / dv4;
+    cv = tid - rv0 * dv4;
+  }
+};
+
+__device__ __forceinline__ int ring_slot(int head, int r, int C) {
+  const int s = head + r;
+  return s >= C ? s - C : s;
+}
+
+template <int KIND, int NT>
+__device__ __forceinline__ void load_records(const ReplayArgs& a, int item, const SeqPtr& p, const Route& rt,
+                                             int tid, const StageMap& m, RecRegs& rr) {
+  constexpr int DK = NT * 16;
+  if (!rt.work) return;
+  const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
+  const int b = item / H, hd = item - b * H;
+  const int64_t bh = (int64_t)b * H + hd;
+  const float* rk = a.ring_k + bh * (int64_t)C * DK;
+  const float* rv = a.ring_v + bh * (int64_t)C * dv;
+#pragma unroll
+  for (int j = 0; j < kRecK; ++j) {
+    const int r = m.rk0 + j * m.kstep;
+    if (r < R) rr.kb[j] = ld4(rk + ring_slot(p.head, r, C) * DK + 4 * m.ck);
+  }
+#pragma unroll
+  for (int j = 0; j < kRecV; ++j) {
+    const int r = m.rv0 + j * 16;
+    if (r < R) rr.vb[j] = ld4(rv + ring_slot(p.head, r, C) * dv + 4 * m.cv);
+  }
+  if (m.rk0 < T) rr.qv = ld4(a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck);
+  if (tid < R) rr.al = a.ring_alpha[bh * C + ring_slot(p.head, tid, C)];
+  if (KIND == REPLAYSSM_GDN && tid >= p.h && tid < R) rr.be = a.ring_beta[bh * C + ring_slot(p.head, tid, C)];
+}
+
+// The item's rows into LDS: from the registers, and the rows beyond the
+// register passes (windows longer than 3 * nthr / LPR rows) straight from HBM.
 template <int KIND, int NT, int TMAX>
-__global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
+__device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds, int item,
+                                              const SeqPtr& p, const Route& rt, int tid, int nthr,
+                                              const StageMap& m, const RecRegs& rr) {
+  constexpr int DK = NT * 16;
+  const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
+  const int b = item / H, hd = item - b * H;
+  const int64_t bh = (int64_t)b * H + hd;
+  const float* rk = a.ring_k + bh * (int64_t)C * DK;
+  const float* rv = a.ring_v + bh * (int64_t)C * dv;
+  for (int r = m.rk0 + kRecK * m.kstep; r < R; r += m.kstep)
+    st4(sm + lds.k + r * lds.dks + 4 * m.ck, ld4(rk + ring_slot(p.head, r, C) * DK + 4 * m.ck));
+  for (int r = m.rv0 + kRecV * 16; r < R; r += 16)
+    st4(sm + lds.v + r * lds.dvs + 4 * m.cv, ld4(rv + ring_slot(p.head, r, C) * dv + 4 * m.cv));
+  for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
+    st4(sm + lds.q + i * DK + 4 * m.ck, ld4(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
+  for (int r = tid + nthr; r < R; r += nthr) {
+    sm[lds.alpha + r] = a.ring_alpha[bh * C + ring_slot(p.head, r, C)];
+    if (KIND == REPLAYSSM_GDN && r >= p.h) sm[lds.beta + (r - p.h)] = a.ring_beta[bh * C + ring_slot(p.head, r, C)];
+  }
+#pragma unroll
+  for (int j = 0; j < kRecK; ++j) {
+    const int r = m.rk0 + j * m.kstep;
+    if (r < R) st4(sm + lds.k + r * lds.dks + 4 * m.ck, rr.kb[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kRecV; ++j) {
+    const int r = m.rv0 + j * 16;
+    if (r < R) st4(sm + lds.v + r * lds.dvs + 4 * m.cv, rr.vb[j]);
+  }
+  if (m.rk0 < T) st4(sm + lds.q + m.rk0 * DK + 4 * m.ck, rr.qv);
+  for (int i = (m.rk0 < T ? m.rk0 + m.kstep : m.rk0); i < TMAX; i += m.kstep)
+    if (i >= T) st4(sm + lds.q + i * DK + 4 * m.ck, f32x4{0.f, 0.f, 0.f, 0.f});  // rows of absent drafts
+  if (tid < R) sm[lds.alpha + tid] = rr.al;
+  if (KIND == REPLAYSSM_GDN && tid >= p.h && tid < R) sm[lds.beta + (tid - p.h)] = rr.be;
+}
+
+// One item. On entry S holds its early checkpoint copy (decode/verify;
+// requested two items ago) and rr its ring rows (requested during the previous
+// item). On return rr holds (or is loading) the rows of `next` and S the
+// checkpoint of `after_next`, the item after that. Ends with a workgroup
+// barrier after its last LDS read.
+template <int KIND, int NT, int TMAX>
+__device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const int item, const SeqPtr ptr,
+                                            const Route rt, f32x4 (&S)[NT], RecRegs& rr, const int next,
+                                            const SeqPtr nptr, const Route nrt, const int after_next) {
   constexpr int DK = NT * 16;
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
   constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
   constexpr bool GDN = (KIND == REPLAYSSM_GDN);
-  extern __shared__ f32x4 smem_v4[];
-  float* sm = reinterpret_cast<float*>(smem_v4);
 
-  const int tid = threadIdx.x;
+  // The thread index is laundered per item: without it the compiler hoists
+  // every thread-derived address out of the item loop and keeps them all live
+  // across it, which doubles the register footprint and halves occupancy.
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nthr = blockDim.x;
@@ -47,112 +207,136 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   const int g = lane >> 4;
   const int col = lane & 15;
   const int H = a.H, C = a.C, dv = a.dv;
-  const int b = blockIdx.x / H;
-  const int hd = blockIdx.x - b * H;
+  const int b = item / H;
+  const int hd = item - b * H;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
   const ReplayLds lds(C, DK, dv, TMAX);
+  const StageMap map(tid, nthr, LPR, dv);
 
-  const int head = a.head[b];
-  const int hc = a.h[b];
-  const int pend = a.p[b];
   const int mode = a.mode;
-  const int T = (mode == kModeFlush) ? 0 : a.T;
-  // pointers outside their invariant ranges would address outside the ring
-  const bool corrupt = head < 0 || head >= C || hc < 0 || hc > a.L || pend < 0 || pend > C - a.L;
-  const bool bad = corrupt || ((mode != kModeFlush) && (pend != T));
-  const bool fold = !bad && ((mode == kModeFlush) ? (hc > 0) : (hc + T > a.L));
-  const bool work = !bad && (mode != kModeFlush || fold);
-  const bool outputs = work && (mode != kModeFlush);
-  const int R = hc + T;          // staged records: committed [0, hc), drafts [hc, hc + T)
-  const int r0 = fold ? hc : 0;  // first record replayed on top of the checkpoint
   const int prec = a.precision;
-  const bool read_lp =
-      (prec == REPLAYSSM_BF16_SHARED) || (prec == REPLAYSSM_FP32_HP_BF16_LP && !fold);
+  const int64_t hoff = bh * (int64_t)(dv * DK);
 
-  // ---- 1. checkpoint into registers, records into LDS -----------------------
-  f32x4 S[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (work) {
-    const int64_t hoff = bh * (int64_t)(dv * DK);
-    if (!read_lp) {
-      const float* src = a.hp + hoff + (int64_t)(wave * NT) * 256 + lane * 4;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[nt] = ld4(src + nt * 256);
+  // The pointers were read before this item started (in the workgroup's
+  // batch read); this kernel never writes them.
+  const int head = ptr.head;
+  const int hc = ptr.h;
+  const int T = rt.T;
+  const bool corrupt = rt.corrupt, bad = rt.bad, fold = rt.fold, work = rt.work, outputs = rt.outputs;
+  const int R = rt.R, r0 = rt.r0;
+
+  // ---- 1. checkpoint and records ----------------------------------------------
+  if (fold && (mode == kModeFlush || prec == REPLAYSSM_FP32_HP_BF16_LP)) {
+    if (prec != REPLAYSSM_BF16_SHARED) {
+      load_hp<NT>(a.hp + hoff, wave, lane, S);
     } else if constexpr (NT >= 2) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.lp + hoff) + (wave * NT / 2) * 64 + lane;
-#pragma unroll
-      for (int m = 0; m < NT / 2; ++m) unpack_lp_chunk(src[m * 64], S[2 * m], S[2 * m + 1]);
-    }
-
-    const float* rk = a.ring_k + bh * (int64_t)C * DK;
-    const float* rv = a.ring_v + bh * (int64_t)C * dv;
-    {  // k rows: LPR threads per row
-      const int r_in = tid / LPR, c4 = tid % LPR;
-      for (int r = r_in; r < R; r += nthr / LPR) {
-        int slot = head + r;
-        if (slot >= C) slot -= C;
-        st4(sm + lds.k + r * lds.dks + 4 * c4, ld4(rk + slot * DK + 4 * c4));
-      }
-    }
-    {  // v rows: dv / 4 threads per row (nthr = 16 * dv / 4)
-      const int dv4 = dv >> 2;
-      const int r_in = tid / dv4, c4 = tid - (tid / dv4) * dv4;
-      for (int r = r_in; r < R; r += 16) {
-        int slot = head + r;
-        if (slot >= C) slot -= C;
-        st4(sm + lds.v + r * lds.dvs + 4 * c4, ld4(rv + slot * dv + 4 * c4));
-      }
-    }
-    for (int r = tid; r < R; r += nthr) {
-      int slot = head + r;
-      if (slot >= C) slot -= C;
-      sm[lds.alpha + r] = a.ring_alpha[bh * C + slot];
-      if (GDN && r >= hc) sm[lds.beta + (r - hc)] = a.ring_beta[bh * C + slot];
-    }
-    for (int idx = tid; idx < TMAX * LPR; idx += nthr) {
-      const int i = idx / LPR, c4 = idx % LPR;
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (i < T) x = ld4(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * c4);
-      st4(sm + lds.q + i * DK + 4 * c4, x);
+      load_lp<NT>(a.lp + hoff, wave, lane, S);
     }
   }
+  if (work) store_records<KIND, NT, TMAX>(a, sm, lds, item, ptr, rt, tid, nthr, map, rr);
   __syncthreads();
 
-  // ---- 2. decay products and record dot products -----------------------------
-  if (outputs) {
-    // Row r + 1 of gq / gk, for r in [r0 - 1, R): gq[.][i] = prod of alpha over
-    // records (r, hc + i] (decay of record r at draft i), gk[.][i] the same over
-    // (r, hc + i - 1] (the state just before draft i). Row r0 (r = r0 - 1) thus
-    // holds the checkpoint's factors Gamma_i and Gamma_{i-1}. Entries for
-    // records that come after the draft stay zero.
-    for (int t = tid; t < R - r0 + 1; t += nthr) {
-      const int r = r0 - 1 + t;
-      float* gq = sm + lds.gq + (r + 1) * TMAX;
-      float* gk = sm + lds.gk + (r + 1) * TMAX;
+  // ---- the next item's ring rows: requested now, waited for by the next item
+  const bool more = next < a.B * a.H;
+  if (more) load_records<KIND, NT>(a, next, nptr, nrt, tid, map, rr);
+
+  // ---- matvecs y_i = S q_i (and S k_i for GDN), lane-partial over its columns.
+  // A replay item does them right away, which frees S for the checkpoint two
+  // items ahead (the other buffer already holds the next item's). A fold item
+  // does them on the folded state, further down.
+  const bool prefetch = after_next < a.B * a.H && mode != kModeFlush;
+  if (!work && prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
+  float yq[TMAX], yk[TMAX];
+#pragma unroll
+  for (int i = 0; i < TMAX; ++i) {
+    yq[i] = 0.f;
+    yk[i] = 0.f;
+  }
+  auto matvec = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
-        gq[i] = 0.f;
-        gk[i] = 0.f;
+        if (i < T) {
+          yq[i] += dot4(S[nt], ld4(sm + lds.q + i * DK + nt * 16 + 4 * g));
+          if (GDN) yk[i] += dot4(S[nt], ld4(sm + lds.k + (hc + i) * lds.dks + nt * 16 + 4 * g));
+        }
       }
-      float prod = 1.f;
-      for (int rr = r + 1; rr < R; ++rr) {
-        const int i = rr - hc;
-        if (i >= 0) gk[i] = prod;
-        prod *= sm[lds.alpha + rr];
-        if (i >= 0) gq[i] = prod;
-      }
-      if (r >= hc) gq[r - hc] = 1.f;
     }
+  };
+  if (outputs && !fold) {
+    matvec();
+    if (prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
   }
-  if (fold) {
-    // gf[t] = prod of alpha over committed records [t, hc): gf[0] = Gamma_h
-    // scales the checkpoint, gf[j + 1] weighs record j in the fold.
-    for (int t = tid; t <= hc; t += nthr) {
-      float prod = 1.f;
-      for (int rr = t; rr < hc; ++rr) prod *= sm[lds.alpha + rr];
-      sm[lds.gf + t] = prod;
+
+  // ---- 2. decay products and record dot products -----------------------------
+  // gq[r + 1][i] = prod of alpha over records (r, hc + i]: the decay of record r
+  // at draft i; gk[r + 1][i] the same over (r, hc + i - 1]: at the state just
+  // before draft i. Row r0 (r = r0 - 1) holds the checkpoint's factors Gamma_i
+  // and Gamma_{i-1}. Entries of records after the end point are zero.
+  // gf[t] = prod of alpha over committed records [t, hc): gf[0] = Gamma_h
+  // scales the checkpoint in a fold, gf[j + 1] weighs record j.
+  // Each product set is one suffix-product scan across a wavefront (lane l
+  // stands for record first + l), one wavefront per end point.
+  if (work) {
+    const bool wide = (R - r0 + 1 > kWave) || (hc + 1 > kWave);
+    if (!wide) {
+      const int njobs = (outputs ? 2 * T : 0) + (fold ? 1 : 0);
+      for (int job = wave; job < njobs; job += W) {
+        int first, e, last;
+        float* out;
+        int stride;
+        if (job < 2 * T && outputs) {
+          const int i = job >> 1;
+          first = r0 - 1;
+          last = R - 1;
+          e = (job & 1) ? hc + i - 1 : hc + i;
+          out = sm + ((job & 1) ? lds.gk : lds.gq) + i;
+          stride = TMAX;
+        } else {
+          first = -1;
+          last = hc - 1;
+          e = hc - 1;
+          out = sm + lds.gf;
+          stride = 1;
+        }
+        const int r = first + lane;
+        float x = (r + 1 <= e) ? sm[lds.alpha + r + 1] : 1.f;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const float y = __shfl_down(x, d, kWave);
+          if (lane + d < kWave) x *= y;
+        }
+        if (r <= last) out[(r + 1) * stride] = (r <= e) ? x : 0.f;
+      }
+    } else {
+      if (outputs) {
+        for (int t = tid; t < R - r0 + 1; t += nthr) {
+          const int r = r0 - 1 + t;
+          float* gq = sm + lds.gq + (r + 1) * TMAX;
+          float* gk = sm + lds.gk + (r + 1) * TMAX;
+          for (int i = 0; i < TMAX; ++i) {
+            gq[i] = 0.f;
+            gk[i] = 0.f;
+          }
+          float prod = 1.f;
+          for (int rr = r + 1; rr < R; ++rr) {
+            const int i = rr - hc;
+            if (i >= 0) gk[i] = prod;
+            prod *= sm[lds.alpha + rr];
+            if (i >= 0) gq[i] = prod;
+          }
+          if (r >= hc) gq[r - hc] = 1.f;
+        }
+      }
+      if (fold) {
+        for (int t = tid; t <= hc; t += nthr) {
+          float prod = 1.f;
+          for (int rr = t; rr < hc; ++rr) prod *= sm[lds.alpha + rr];
+          sm[lds.gf + t] = prod;
+        }
+      }
     }
   }
   if (outputs) {
@@ -205,43 +389,16 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
         S[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval, S[nt], 0, 0, 0);
       }
     }
-    const int64_t hoff = bh * (int64_t)(dv * DK);
-    if (prec != REPLAYSSM_BF16_SHARED) {
-      float* dst = a.hp + hoff + (int64_t)(wave * NT) * 256 + lane * 4;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) st4(dst + nt * 256, S[nt]);
-    }
+    if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, S);
     if constexpr (NT >= 2) {
-      if (prec != REPLAYSSM_FP32) {
-        uint4* dst = reinterpret_cast<uint4*>(a.lp + hoff) + (wave * NT / 2) * 64 + lane;
-#pragma unroll
-        for (int m = 0; m < NT / 2; ++m) {
-          const uint4 x = pack_lp_chunk(S[2 * m], S[2 * m + 1]);
-          dst[m * 64] = x;
-          if (prec == REPLAYSSM_BF16_SHARED) unpack_lp_chunk(x, S[2 * m], S[2 * m + 1]);
-        }
-      }
+      if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, S, prec == REPLAYSSM_BF16_SHARED);
     }
+    if (outputs) matvec();
+    if (prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
   }
 
   // ---- 4/5. outputs of the drafts ---------------------------------------------
   if (outputs) {
-    float yq[TMAX], yk[TMAX];
-#pragma unroll
-    for (int i = 0; i < TMAX; ++i) {
-      yq[i] = 0.f;
-      yk[i] = 0.f;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int i = 0; i < TMAX; ++i) {
-        if (i < T) {
-          yq[i] += dot4(S[nt], ld4(sm + lds.q + i * DK + nt * 16 + 4 * g));
-          if (GDN) yk[i] += dot4(S[nt], ld4(sm + lds.k + (hc + i) * lds.dks + nt * 16 + 4 * g));
-        }
-      }
-    }
     const float* gq = sm + lds.gq;
     const float* gk = sm + lds.gk;
     const float* cq = sm + lds.cq;
@@ -303,37 +460,138 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
     }
   }
 
-  // ---- 6. pointers ------------------------------------------------------------
+  // The item's last LDS reads are done once every wavefront is here.
   __syncthreads();
-  if (tid == 0 && arrive_last(a.arrive, b, H)) {
-    if (bad) {
-      atomicOr(a.err, corrupt ? REPLAYSSM_DEVERR_CORRUPT : REPLAYSSM_DEVERR_PENDING);
-    } else {
-      int nhead = head, nh = hc;
-      int64_t nf = a.folded[b];
-      if (fold) {
-        nhead = head + hc;
-        if (nhead >= C) nhead -= C;
-        nf += hc;
-        nh = 0;
-      }
-      if (mode == kModeDecode) {
-        nh += 1;
-        a.p[b] = 0;
-      }
-      a.head[b] = nhead;
-      a.h[b] = nh;
-      a.folded[b] = nf;
+}
+
+// Persistent workgroups: each one walks the (sequence, head) items with a
+// stride of the grid size, so that the machine is filled once with as many
+// workgroups as fit and none pays a launch per head; consecutive items of the
+// grid are neighbours in memory, so the stream over the checkpoints stays
+// sequential.
+// Checkpoint prefetch depth (1: the next item's; 2: also the one after, in a
+// second register buffer). Two buffers keep more bytes in flight per
+// workgroup but cost registers, hence occupancy.
+template <int KIND, int NT, int TMAX>
+constexpr int prefetch_depth() {
+  return REPLAYSSM_PREFETCH_DEPTH;
+}
+
+template <int KIND, int NT, int TMAX>
+__global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
+  constexpr int DEPTH = prefetch_depth<KIND, NT, TMAX>();
+  extern __shared__ f32x4 smem_v4[];
+  float* sm = reinterpret_cast<float*>(smem_v4);
+  const int items = a.B * a.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= items) return;
+  // Pointers of the workgroup's items are read 64 at a time, one item per
+  // lane, and handed to each item with readlane: no memory round trip per item.
+  int ph = 0, phc = 0, pp = 0;
+  auto batch = [&](int first_item) {
+    const int it = first_item + lane * G;
+    if (it < items) {
+      const int bb = it / a.H;
+      ph = a.head[bb];
+      phc = a.h[bb];
+      pp = a.p[bb];
     }
+  };
+  auto ptr_at = [&](int kl) {
+    return SeqPtr{__builtin_amdgcn_readlane(ph, kl), __builtin_amdgcn_readlane(phc, kl),
+                  __builtin_amdgcn_readlane(pp, kl)};
+  };
+  batch(blockIdx.x);
+  SeqPtr ptr = ptr_at(0);
+  Route rt = route_of(a, ptr);
+  // With two checkpoint buffers they are used alternately (the loop body is
+  // unrolled by two so that each has fixed registers): while one item
+  // computes, the next item's checkpoint and the one after it are in flight.
+  f32x4 SA[NT], SB[DEPTH == 2 ? NT : 1];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) SA[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DEPTH == 2) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) SB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  RecRegs rr;
+  {
+    const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
+    load_records<KIND, NT>(a, blockIdx.x, ptr, rt, threadIdx.x, map, rr);
+  }
+  if (a.mode != kModeFlush) {
+    load_ckpt_early<NT>(a, blockIdx.x, wave, lane, SA);
+    if constexpr (DEPTH == 2)
+      if ((int)blockIdx.x + G < items) load_ckpt_early<NT>(a, blockIdx.x + G, wave, lane, SB);
+  }
+  auto step = [&](int k, int item, f32x4 (&S)[NT]) {
+    const int next = item + G;
+    const int kn = (k + 1) & 63;
+    if (kn == 0 && next < items) batch(next);
+    const SeqPtr nptr = ptr_at(kn);
+    const Route nrt = route_of(a, nptr);
+    replay_item<KIND, NT, TMAX>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt, DEPTH == 2 ? next + G : next);
+    ptr = nptr;
+    rt = nrt;
+  };
+  if constexpr (DEPTH == 2) {
+    for (int k = 0, item = blockIdx.x; item < items; k += 2, item += 2 * G) {
+      step(k, item, SA);
+      if (item + G >= items) break;
+      step(k + 1, item + G, SB);
+    }
+  } else {
+    for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) step(k, item, SA);
+  }
+}
+
+// Advances every sequence's pointers after a decode / verify / flush launch,
+// with the same route rule the replay kernel applied to the same (old) values:
+// a fold moves head past the folded records and adds them to `folded`; decode
+// then commits its token (h += 1, p = 0). Sequences the replay kernel skipped
+// set their error bit and keep their pointers. One thread per sequence; a
+// separate launch, so that the replay kernel never writes what its other
+// workgroups read (a per-sequence arrival counter instead costs far more: its
+// atomics serialise on one address per sequence).
+__global__ void __launch_bounds__(256) commit_kernel(const ReplayArgs a) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= a.B) return;
+  const SeqPtr p{a.head[b], a.h[b], a.p[b]};
+  const Route rt = route_of(a, p);
+  if (rt.bad) {
+    atomicOr(a.err, rt.corrupt ? REPLAYSSM_DEVERR_CORRUPT : REPLAYSSM_DEVERR_PENDING);
+    return;
+  }
+  int head = p.head, h = p.h;
+  if (rt.fold) {
+    head += h;
+    if (head >= a.C) head -= a.C;
+    a.folded[b] += h;
+    h = 0;
+  }
+  if (a.mode == kModeDecode) {
+    h += 1;
+    a.p[b] = 0;
+  }
+  a.head[b] = head;
+  a.h[b] = h;
 }
 
 template <int KIND, int NT, int TMAX>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
   const ReplayLds lds(a.C, NT * 16, a.dv, TMAX);
-  const dim3 grid((unsigned)(a.B * a.H));
-  const dim3 block((unsigned)(a.dv / 16 * kWave));
-  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX>), grid, block, (size_t)lds.total * 4, s, a);
+  const int block = a.dv / 16 * kWave;
+  const size_t smem = (size_t)lds.total * 4;
+  int grid = 0;
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX>), block,
+                                 smem, a.B * a.H, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX>), dim3((unsigned)grid), dim3((unsigned)block), smem, s,
+                     a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,8 +1,48 @@
 // Buffer and pointer kernels of libreplayssm: append, accept, init, and the
 // conversions between the logical checkpoint order and the private layouts.
+#include <mutex>
+#include <vector>
+
 #include "device.hpp"
 
 namespace rs {
+
+hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid) {
+  struct Entry {
+    const void* kernel;
+    int block;
+    size_t smem;
+    int device;
+    int per_cu;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  static int cus[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int per_cu = -1;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+      e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+    }
+    for (const Entry& x : cache)
+      if (x.kernel == kernel && x.block == block && x.smem == smem && x.device == dev) per_cu = x.per_cu;
+    if (per_cu < 0) {
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, smem);
+      if (e != hipSuccess) return e;
+      if (per_cu < 1) per_cu = 1;
+      cache.push_back(Entry{kernel, block, smem, dev, per_cu});
+    }
+  }
+  const long g = (long)cus[dev] * per_cu;
+  *grid = (int)(g < items ? g : items);
+  if (*grid < 1) *grid = 1;
+  return hipSuccess;
+}
 
 // Append: the T new records of every head of sequence b go to ring slots
 // (head + h + p + i) mod C ("ReplaySSM: Cache SSM Inputs, Not State", How it

@@ -98,3 +98,22 @@ def test_explicit_flush_mid_run(kind):
     assert r.check_checkpoint() <= TOL
     assert r.error_word() == 0
     assert r.report.max_rel <= TOL and r.report.max_rel_u <= TOL
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_wide_window_standard(kind):
+    """L = 64 with one wavefront per workgroup: more records than lanes (serial decay path,
+    staging tail loop, alpha tail)."""
+    sh = LayerShape(kind, 2, 3, 16, 32)
+    r = Runner(sh, 64, 1, wid=60, decay="slow")
+    rep = run_standard(r, 140)
+    _assert_clean(rep)
+    assert rep.folds == 2 * 2
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_wide_window_spec(kind):
+    sh = LayerShape(kind, 3, 2, 32, 32)
+    r = Runner(sh, 56, 8, wid=61, decay="slow")
+    rep = run_spec(r, 8, 24)
+    _assert_clean(rep)
