@@ -38,6 +38,33 @@ HBM_PEAK_GBS = 8000.0
 POOL_BYTES_MAX = 8 << 30
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "replay_kernel_mamba2_decode_b256_pmc.md")
+KERNEL_SOURCES = ["ssm_decode_amd/csrc/replay.hip", "ssm_decode_amd/csrc/device.hpp",
+                  "ssm_decode_amd/csrc/internal.hpp"]
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None when the
+    kernel sources have changed since the counters were taken."""
+    import hashlib
+
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "kernel_sources_sha16"):
+            k, v = line.strip().split(":", 1)
+            vals[k] = v.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if vals.get("kernel_sources_sha16") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,7 +390,8 @@ def main():
         "config": {"workload": w.name, "kind": sh.kind, "B": sh.B, "H": sh.H, "P": sh.P, "N": sh.N, "L": w.L,
                    "T": 1, "precision": w.precision, "state_MiB_per_seq": sh.H * sh.P * sh.N * 4 / 2**20},
         "roofline": {"bound": "hbm", "kernel": "replay_kernel (decode)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(), "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "avg_launch_us": main_res["kernel_avg_us"],
                      "algorithmic_bytes_per_launch": main_res["kernel_bytes"] / main_res["kernel_launches"],
                      "plain_step_us": main_res["plain_avg_us"], "fold_step_us": main_res["fold_avg_us"],

@@ -8,7 +8,9 @@ so both sides see identical numbers.
 
 Error metric, per output vector o (one draft of one head):
     rel = max|o_gpu - o_ref| / max(max|o_ref|, 1e-30)
-and a run reports the maximum over all compared vectors.
+and a run reports the maximum over all compared vectors. When whole sequences
+are followed, the same metric is also taken per (sequence, draft) over the
+token's whole layer output (all heads), the vector the bf16-read bar applies to.
 """
 from __future__ import annotations
 
@@ -33,6 +35,7 @@ def rel_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
 @dataclass
 class Report:
     max_rel: float = 0.0
+    max_rel_token: float = 0.0  # per (sequence, draft): the layer output over every followed head
     max_rel_u: float = 0.0
     max_rel_ckpt: float = 0.0
     rels: List[float] = field(default_factory=list)
@@ -48,6 +51,15 @@ class Report:
         if r.size:
             self.max_rel = max(self.max_rel, float(r.max()))
             self.rels.append(float(np.percentile(r, 99.9)))
+
+    def update_token(self, r: np.ndarray) -> None:
+        if r.size:
+            self.max_rel_token = max(self.max_rel_token, float(r.max()))
+
+
+def whole_sequences(B: int, H: int, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+    """Every head of the listed sequences (so that a token's whole layer output is followed)."""
+    return [(b, h) for b in sorted(set(seqs)) if 0 <= b < B for h in range(H)]
 
 
 def sample_heads(B: int, H: int, n: int, seed: int = 0) -> List[Tuple[int, int]]:
@@ -82,6 +94,10 @@ class Runner:
         self.oracle = OracleSession(shape.kind, shape.B, shape.H, shape.P, shape.N, L, T_max, S0h, self.heads)
         self.report = Report()
         self.step_id = 0
+        # token metric only when whole sequences are followed, in (b, h) order
+        seqs = sorted({b for b, _ in self.heads})
+        self.token_groups = (len(self.heads) == len(seqs) * shape.H and
+                             self.heads == [(b, h) for b in seqs for h in range(shape.H)])
 
     # -- inputs --------------------------------------------------------------
     def inputs(self, T: int) -> Dict[str, torch.Tensor]:
@@ -129,12 +145,21 @@ class Runner:
         rs.decode(self.cfg, self.layer.struct, x["q"], out)
         ref, u, folds = self.oracle.decode(self._sel(x["q"]))
         got = self._sel(out)
-        self.report.update(rel_err(got, ref).ravel())
+        self._score(got, ref)
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
             self._check_u(u, 1)
         return got
+
+    def _score(self, got: np.ndarray, ref: np.ndarray) -> None:
+        self.report.update(rel_err(got, ref).ravel())
+        if self.token_groups:
+            H, P = self.shape.H, self.shape.P
+            T = got.shape[1]
+            g = got.reshape(-1, H, T, P).transpose(0, 2, 1, 3).reshape(-1, T, H * P)
+            r = ref.reshape(-1, H, T, P).transpose(0, 2, 1, 3).reshape(-1, T, H * P)
+            self.report.update_token(rel_err(g, r).ravel())
 
     def verify(self, x: Dict[str, torch.Tensor], T: int) -> np.ndarray:
         sh = self.shape
@@ -142,7 +167,7 @@ class Runner:
         rs.verify(self.cfg, self.layer.struct, T, x["q"], out)
         ref, u, folds = self.oracle.verify(self._sel(x["q"]))
         got = self._sel(out)
-        self.report.update(rel_err(got, ref).ravel())
+        self._score(got, ref)
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
