@@ -10,11 +10,14 @@ synthetic tensors generated on the GPU before the timed region (a pool of
 distinct steps, cycled when K + W exceeds it). Prints one JSON line:
 
   value      tokens/s of the whole step (B tokens per step), HIP-event timed over
-             K steps after W warm-up steps, inputs already resident in HBM
-  roofline   the decode kernel (the dominant one): algorithmic bytes per launch
-             (checkpoint read, h+1 records, q, output, checkpoint write on fold
-             steps) / its average launch duration, both measured live in a second
-             pass with events around each launch, against 8 TB/s
+             K steps after W warm-up steps, inputs already resident in HBM; a step
+             is one replayssm_decode_step launch (append + decode fused)
+  roofline   that kernel (the only one of the step): algorithmic bytes per launch
+             (checkpoint read, h+1 records, q, output, the new record's ring write,
+             checkpoint write on fold steps) / its average launch duration, both
+             measured live in a second pass with events around each launch, against
+             8 TB/s
+  unfused    the same step as replayssm_append + replayssm_decode
   eager      the conventional kernel that loads and stores the state every step
   workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint
   cpu_baseline  the CPU oracle (fp64 eager recurrence, OpenMP over heads) on a
@@ -97,10 +100,15 @@ def ckpt_write_bytes(precision, P, N):
     return {"fp32": 4 * P * N, "fp32_hp_bf16_lp": 6 * P * N, "bf16_shared": 2 * P * N}[precision]
 
 
-def replay_launch_bytes(kind, precision, P, N, h, T, fold):
-    """Bytes one head moves in one decode/verify launch with h committed records before it."""
+def replay_launch_bytes(kind, precision, P, N, h, T, fold, fused=False):
+    """Bytes one head moves in one decode/verify launch with h committed records before it.
+
+    A fused launch (append + decode / verify) also writes the drafts' records to the ring
+    (k, alpha and v for Mamba-2; k, alpha and beta for GDN, whose u is counted below)."""
     b = ckpt_read_bytes(precision, P, N, fold)
     b += (h + T) * record_bytes(kind, P, N)  # committed records and the drafts' own records
+    if fused:
+        b += T * (record_bytes(kind, P, N) - (4 * P if kind == "gdn" else 0))
     b += T * 4 * N + T * 4 * P  # q in, o out
     if kind == "gdn":
         b += T * 4 * P  # u written back into the ring
@@ -144,8 +152,8 @@ def make_pool(torch, synth, shape, T, n_needed, seed, wid, bytes_per_set):
     return [synth.device_step(seed, wid, 1000 + i, shape, T, "cuda") for i in range(n)]
 
 
-def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True):
-    """Append + decode steps of a standard-decoding workload; returns timing and byte counts."""
+def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True, fused=True):
+    """Standard-decoding steps (fused append + decode launches, or append then decode)."""
     sh = w.shape
     cfg = rs.make_config(sh.kind, w.precision, sh.B, sh.H, sh.P, sh.N, w.L, 1)
     layer = rs.LayerState(cfg)
@@ -157,8 +165,11 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
 
     def step(i):
         x = pool[i % len(pool)]
-        rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
-        rs.decode(cfg, st, x["q"], out, stream)
+        if fused:
+            rs.decode_step(cfg, st, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
+        else:
+            rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+            rs.decode(cfg, st, x["q"], out, stream)
 
     for i in range(warmup):
         step(i)
@@ -171,11 +182,12 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
     h, kbytes, nfold = h0, 0, 0
     for _ in range(steps):
         fold = h + 1 > w.L
-        kbytes += replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold)
+        kbytes += replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold, fused)
         nfold += fold
         h = 1 if fold else h + 1
     res = {"ms": tm.ms, "steps": steps, "tokens": sh.B * steps, "decode_bytes": kbytes * sh.B * sh.H,
-           "append_bytes": append_bytes(sh.kind, sh.P, sh.N, 1) * sh.B * sh.H * steps, "folds": nfold}
+           "append_bytes": 0 if fused else append_bytes(sh.kind, sh.P, sh.N, 1) * sh.B * sh.H * steps,
+           "folds": nfold, "fused": fused}
     if kernel_pass:
         # second pass: events around every decode launch (same stream as the kernels)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -183,16 +195,21 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
         h1 = int(layer.h[0].item())
         for i in range(steps):
             x = pool[(warmup + steps + i) % len(pool)]
-            rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
-            evs[i][0].record(stream)
-            rs.decode(cfg, st, x["q"], out, stream)
-            evs[i][1].record(stream)
+            if fused:
+                evs[i][0].record(stream)
+                rs.decode_step(cfg, st, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
+                evs[i][1].record(stream)
+            else:
+                rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+                evs[i][0].record(stream)
+                rs.decode(cfg, st, x["q"], out, stream)
+                evs[i][1].record(stream)
         torch.cuda.synchronize()
         durs = np.array([a.elapsed_time(b) for a, b in evs])
         h, kb, fold_ms, plain_ms, fold_b, plain_b = h1, 0, [], [], 0, 0
         for i in range(steps):
             fold = h + 1 > w.L
-            bb = replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold) * sh.B * sh.H
+            bb = replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold, fused) * sh.B * sh.H
             kb += bb
             (fold_ms if fold else plain_ms).append(durs[i])
             if fold:
@@ -219,7 +236,7 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
     return res
 
 
-def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, kernel_pass=True):
+def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, kernel_pass=True, fused=True):
     sh = w.shape
     if B is not None:
         sh = synth.LayerShape(sh.kind, B, sh.H, sh.P, sh.N)
@@ -238,10 +255,14 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
 
     def rnd(i, evs=None):
         x = pool[i % len(pool)]
-        rs.append(cfg, st, T, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+        if not fused:
+            rs.append(cfg, st, T, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
         if evs is not None:
             evs[0].record(stream)
-        rs.verify(cfg, st, T, x["q"], out, stream)
+        if fused:
+            rs.verify_step(cfg, st, T, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
+        else:
+            rs.verify(cfg, st, T, x["q"], out, stream)
         if evs is not None:
             evs[1].record(stream)
         rs.accept(cfg, st, accs[i], stream)
@@ -262,7 +283,7 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
         for f in (False, True):
             m = fold == f
             if m.any():
-                kb += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f) for hh in h[m]) * sh.H
+                kb += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f, fused) for hh in h[m]) * sh.H
         h = np.where(fold, 0, h) + acc_host[warmup + i]
     res = {"ms": tm.ms, "rounds": rounds, "accepted_tokens": accepted, "drafts": sh.B * T * rounds,
            "verify_bytes": int(kb)}
@@ -281,7 +302,7 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
             for f in (False, True):
                 m = fold == f
                 if m.any():
-                    kb2 += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f) for hh in h[m]) * sh.H
+                    kb2 += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f, fused) for hh in h[m]) * sh.H
             h = np.where(fold, 0, h) + acc_host[base + i]
         res.update({"kernel_avg_us": float(durs.mean() * 1e3), "kernel_gbs": kb2 / (durs.sum() * 1e6)})
     err = rs.read_error(st)
@@ -389,7 +410,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "kind": sh.kind, "B": sh.B, "H": sh.H, "P": sh.P, "N": sh.N, "L": w.L,
                    "T": 1, "precision": w.precision, "state_MiB_per_seq": sh.H * sh.P * sh.N * 4 / 2**20},
-        "roofline": {"bound": "hbm", "kernel": "replay_kernel (decode)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "replay_kernel (fused append + decode)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(), "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "avg_launch_us": main_res["kernel_avg_us"],
@@ -398,7 +419,13 @@ def main():
                      "plain_step_gbs": main_res["plain_gbs"], "fold_step_gbs": main_res["fold_gbs"],
                      "us_by_h_before_step": main_res["us_by_h"]},
         "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
+        "step": "replayssm_decode_step (append + decode in one launch)",
     }
+    if not args.quick:
+        unf = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False)
+        line["unfused"] = {"tokens_per_s": unf["tokens"] / (unf["ms"] * 1e-3),
+                           "decode_kernel_gbs": unf["kernel_bytes"] / (unf["kernel_ms_total"] * 1e6),
+                           "step": "replayssm_append then replayssm_decode"}
     if not args.quick:
         eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
         line["eager"] = {"tokens_per_s": eg["tokens"] / (eg["ms"] * 1e-3), "gbs": eg["gbs"],

@@ -220,6 +220,22 @@ int replayssm_accept(const replayssm_config* cfg, const replayssm_state* st,
  * alone. Afterwards the checkpoint alone is the state at position `folded`. */
 int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void* stream);
 
+/* The same two calls fused with the append that precedes them, in one launch
+ * (the new records are read from the inputs and written to the ring by the
+ * kernel that replays them, which saves the append launch and the re-read of
+ * the records). Semantics are exactly replayssm_append followed by the
+ * unfused call; p must be 0 on entry (else the sequence is skipped and
+ * flagged REPLAYSSM_DEVERR_PENDING).
+ *   decode_step: alpha, beta [B][H]; k, q [B][H][dk]; v [B][H][dv]; out [B][H][dv]
+ *   verify_step: alpha, beta [B][T][H]; k, q [B][T][H][dk]; v [B][T][H][dv];
+ *                out [B][T][H][dv]; afterwards p = T (accept follows). */
+int replayssm_decode_step(const replayssm_config* cfg, const replayssm_state* st, const float* alpha,
+                          const float* k, const float* v, const float* beta, const float* q, float* out,
+                          void* stream);
+int replayssm_verify_step(const replayssm_config* cfg, const replayssm_state* st, int T, const float* alpha,
+                          const float* k, const float* v, const float* beta, const float* q, float* out,
+                          void* stream);
+
 /* ---- eager comparison kernels -------------------------------------------- */
 
 /* The conventional decode step the method is measured against ("How it

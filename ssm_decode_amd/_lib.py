@@ -68,6 +68,9 @@ SIGNATURES = {
     "replayssm_append": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp],
     "replayssm_decode": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp, _vp],
     "replayssm_verify": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
+    "replayssm_decode_step": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "replayssm_verify_step": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _vp],
     "replayssm_accept": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp],
     "replayssm_flush": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp],
     "replayssm_eager_step": [ctypes.POINTER(Config), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -179,6 +182,16 @@ def decode(cfg, st, q, out, stream=None):
 def verify(cfg, st, T, q, out, stream=None):
     _check(lib().replayssm_verify(ctypes.byref(cfg), ctypes.byref(st), int(T), _f32(q), _f32(out),
                                   _s(stream)), "verify")
+
+
+def decode_step(cfg, st, alpha, k, v, beta, q, out, stream=None):
+    _check(lib().replayssm_decode_step(ctypes.byref(cfg), ctypes.byref(st), _f32(alpha), _f32(k), _f32(v),
+                                       _f32(beta), _f32(q), _f32(out), _s(stream)), "decode_step")
+
+
+def verify_step(cfg, st, T, alpha, k, v, beta, q, out, stream=None):
+    _check(lib().replayssm_verify_step(ctypes.byref(cfg), ctypes.byref(st), int(T), _f32(alpha), _f32(k),
+                                       _f32(v), _f32(beta), _f32(q), _f32(out), _s(stream)), "verify_step")
 
 
 def accept(cfg, st, accepted, stream=None):

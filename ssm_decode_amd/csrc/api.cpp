@@ -105,6 +105,11 @@ rs::ReplayArgs replay_args(const replayssm_config* c, const replayssm_state* s, 
   a.err = s->err;
   a.q = q;
   a.out = out;
+  a.in_alpha = nullptr;
+  a.in_beta = nullptr;
+  a.in_k = nullptr;
+  a.in_v = nullptr;
+  a.fused = 0;
   a.B = c->B;
   a.H = c->H;
   a.dv = c->dv;
@@ -257,6 +262,39 @@ int replayssm_verify(const replayssm_config* cfg, const replayssm_state* st, int
   const rs::ReplayArgs a = replay_args(cfg, st, T, rs::kModeVerify, q, out);
   return hip_result(rs::launch_replay(cfg->kind, cfg->dk, tmax_bucket(T), a, as_stream(stream)),
                     "verify");
+}
+
+static int fused_call(const replayssm_config* cfg, const replayssm_state* st, int T, int mode,
+                      const float* alpha, const float* k, const float* v, const float* beta, const float* q,
+                      float* out, void* stream, const char* what) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
+  NEED(alpha);
+  NEED(k);
+  NEED(v);
+  NEED(q);
+  NEED(out);
+  if (cfg->kind == REPLAYSSM_GDN) NEED(beta);
+  rs::ReplayArgs a = replay_args(cfg, st, T, mode, q, out);
+  a.in_alpha = alpha;
+  a.in_beta = cfg->kind == REPLAYSSM_GDN ? beta : nullptr;
+  a.in_k = k;
+  a.in_v = v;
+  a.fused = 1;
+  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, tmax_bucket(T), a, as_stream(stream)), what);
+}
+
+int replayssm_decode_step(const replayssm_config* cfg, const replayssm_state* st, const float* alpha,
+                          const float* k, const float* v, const float* beta, const float* q, float* out,
+                          void* stream) {
+  return fused_call(cfg, st, 1, rs::kModeDecode, alpha, k, v, beta, q, out, stream, "decode_step");
+}
+
+int replayssm_verify_step(const replayssm_config* cfg, const replayssm_state* st, int T, const float* alpha,
+                          const float* k, const float* v, const float* beta, const float* q, float* out,
+                          void* stream) {
+  return fused_call(cfg, st, T, rs::kModeVerify, alpha, k, v, beta, q, out, stream, "verify_step");
 }
 
 int replayssm_accept(const replayssm_config* cfg, const replayssm_state* st,

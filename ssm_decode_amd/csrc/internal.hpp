@@ -38,9 +38,9 @@ enum Mode : int { kModeDecode = 0, kModeVerify = 1, kModeFlush = 2 };
 struct ReplayArgs {
   float* hp;
   uint16_t* lp;
-  const float* ring_alpha;
-  const float* ring_beta;
-  const float* ring_k;
+  float* ring_alpha;
+  float* ring_beta;
+  float* ring_k;
   float* ring_v;
   int32_t* head;
   int32_t* h;
@@ -50,6 +50,13 @@ struct ReplayArgs {
   int32_t* err;
   const float* q;  // [B][T][H][dk]
   float* out;      // [B][T][H][dv]
+  // fused append: the T new records come from these inputs (and are written to
+  // the ring by the same launch) instead of from the ring; p must be 0 on entry
+  const float* in_alpha;  // [B][T][H]
+  const float* in_beta;   // [B][T][H] (GDN)
+  const float* in_k;      // [B][T][H][dk]
+  const float* in_v;      // [B][T][H][dv]
+  int fused;
   int B, H, dv, L, C, T;
   int precision;
   int mode;

@@ -28,8 +28,8 @@
 //  5. GDN: u_i = beta_i (v_i - alpha_i S_{i-1} k_i) with S_{i-1} k_i rebuilt
 //     from S k_i and the buffer ("How it works": Gated DeltaNet), sequential
 //     over the drafts, and stored in place of v_i;
-//  6. the pointers are left alone: the commit kernel, launched right after
-//     this one, advances them (they are read, never written, here).
+//  6. the pointers are only read while items run; the last workgroup of the
+//     grid to finish advances them for every sequence.
 //
 // Pipelining: right after step 1 the workgroup requests the next item's ring
 // records (into registers), and as soon as this item's mat-vecs have consumed
@@ -66,7 +66,8 @@ __device__ __forceinline__ Route route_of(const ReplayArgs& a, const SeqPtr& p) 
   Route r;
   r.T = (a.mode == kModeFlush) ? 0 : a.T;
   r.corrupt = p.head < 0 || p.head >= a.C || p.h < 0 || p.h > a.L || p.p < 0 || p.p > a.C - a.L;
-  r.bad = r.corrupt || ((a.mode != kModeFlush) && (p.p != r.T));
+  // decode/verify consume T pending drafts; the fused calls append them first (p = 0 on entry)
+  r.bad = r.corrupt || ((a.mode != kModeFlush) && (p.p != (a.fused ? 0 : r.T)));
   r.fold = !r.bad && ((a.mode == kModeFlush) ? (p.h > 0) : (p.h + r.T > a.L));
   r.work = !r.bad && (a.mode != kModeFlush || r.fold);
   r.outputs = r.work && (a.mode != kModeFlush);
@@ -91,8 +92,10 @@ __device__ __forceinline__ void load_ckpt_early(const ReplayArgs& a, int item, i
 
 // One item's ring rows while they are in flight: up to kRecK k-row and kRecV
 // v-row passes per thread (a pass is nthr / (dk / 4) k rows or 16 v rows), the
-// thread's float4 of the drafts' q, and its alpha / beta.
-constexpr int kRecK = 3, kRecV = 2;
+// thread's float4 of the drafts' q, and its alpha / beta. With dk = 128 and
+// dv >= 64 this covers the L <= 16 rows of every non-fold item; the extra rows
+// of a fold item (up to L + T) go through the tail loop of store_records.
+constexpr int kRecK = 2, kRecV = 1;
 struct RecRegs {
   f32x4 kb[kRecK], vb[kRecV], qv;
   float al, be;
@@ -117,68 +120,136 @@ __device__ __forceinline__ int ring_slot(int head, int r, int C) {
   return s >= C ? s - C : s;
 }
 
-template <int KIND, int NT>
+// Source rows of one item: committed records from the ring; the drafts from
+// the ring too, or, in a fused call, straight from the caller's inputs.
+struct RowSrc {
+  const float* rk;   // ring k rows of the head
+  const float* rv;   // ring v rows
+  const float* ik;   // input k of draft 0 (fused), stride H * dk per draft
+  const float* iv;   // input v of draft 0 (fused), stride H * dv per draft
+  int64_t ia;        // index of draft 0 in the alpha / beta inputs, stride H per draft
+  int64_t bhC;       // first ring slot index of the head
+};
+
+template <int NT>
+__device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) {
+  constexpr int DK = NT * 16;
+  const int H = a.H, C = a.C, dv = a.dv;
+  const int b = item / H, hd = item - b * H;
+  const int64_t bh = (int64_t)b * H + hd;
+  RowSrc s;
+  s.rk = a.ring_k + bh * (int64_t)C * DK;
+  s.rv = a.ring_v + bh * (int64_t)C * dv;
+  s.ia = (int64_t)b * T * H + hd;
+  s.ik = a.in_k + s.ia * DK;
+  s.iv = a.in_v + s.ia * dv;
+  s.bhC = bh * C;
+  return s;
+}
+
+template <int KIND, int NT, bool FUSED>
 __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, const SeqPtr& p, const Route& rt,
                                              int tid, const StageMap& m, RecRegs& rr) {
   constexpr int DK = NT * 16;
   if (!rt.work) return;
   const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
   const int b = item / H, hd = item - b * H;
-  const int64_t bh = (int64_t)b * H + hd;
-  const float* rk = a.ring_k + bh * (int64_t)C * DK;
-  const float* rv = a.ring_v + bh * (int64_t)C * dv;
+  const RowSrc s = row_src<NT>(a, item, T);
+  constexpr bool fused = FUSED;
 #pragma unroll
   for (int j = 0; j < kRecK; ++j) {
     const int r = m.rk0 + j * m.kstep;
-    if (r < R) rr.kb[j] = ld4(rk + ring_slot(p.head, r, C) * DK + 4 * m.ck);
+    if (r < R)
+      rr.kb[j] = ld4((fused && r >= p.h) ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck
+                                         : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck);
   }
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
     const int r = m.rv0 + j * 16;
-    if (r < R) rr.vb[j] = ld4(rv + ring_slot(p.head, r, C) * dv + 4 * m.cv);
+    if (r < R)
+      rr.vb[j] = ld4((fused && r >= p.h) ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
+                                         : s.rv + ring_slot(p.head, r, C) * dv + 4 * m.cv);
   }
   if (m.rk0 < T) rr.qv = ld4(a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck);
-  if (tid < R) rr.al = a.ring_alpha[bh * C + ring_slot(p.head, tid, C)];
-  if (KIND == REPLAYSSM_GDN && tid >= p.h && tid < R) rr.be = a.ring_beta[bh * C + ring_slot(p.head, tid, C)];
+  if (tid < R) {
+    rr.al = (fused && tid >= p.h) ? a.in_alpha[s.ia + (int64_t)(tid - p.h) * H]
+                                  : a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)];
+    if (KIND == REPLAYSSM_GDN && tid >= p.h)
+      rr.be = fused ? a.in_beta[s.ia + (int64_t)(tid - p.h) * H] : a.ring_beta[s.bhC + ring_slot(p.head, tid, C)];
+  }
 }
 
 // The item's rows into LDS: from the registers, and the rows beyond the
-// register passes (windows longer than 3 * nthr / LPR rows) straight from HBM.
-template <int KIND, int NT, int TMAX>
+// register passes straight from HBM.
+// A fused call also writes the drafts' records into their ring slots (k,
+// alpha, and v for Mamba-2 / beta for GDN, whose u replaces v later).
+template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds, int item,
                                               const SeqPtr& p, const Route& rt, int tid, int nthr,
                                               const StageMap& m, const RecRegs& rr) {
   constexpr int DK = NT * 16;
+  constexpr bool GDN = (KIND == REPLAYSSM_GDN);
   const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
   const int b = item / H, hd = item - b * H;
-  const int64_t bh = (int64_t)b * H + hd;
-  const float* rk = a.ring_k + bh * (int64_t)C * DK;
-  const float* rv = a.ring_v + bh * (int64_t)C * dv;
-  for (int r = m.rk0 + kRecK * m.kstep; r < R; r += m.kstep)
-    st4(sm + lds.k + r * lds.dks + 4 * m.ck, ld4(rk + ring_slot(p.head, r, C) * DK + 4 * m.ck));
-  for (int r = m.rv0 + kRecV * 16; r < R; r += 16)
-    st4(sm + lds.v + r * lds.dvs + 4 * m.cv, ld4(rv + ring_slot(p.head, r, C) * dv + 4 * m.cv));
+  const RowSrc s = row_src<NT>(a, item, T);
+  constexpr bool fused = FUSED;
+  float* wk = a.ring_k + (s.rk - a.ring_k);
+  float* wv = a.ring_v + (s.rv - a.ring_v);
+  for (int r = m.rk0 + kRecK * m.kstep; r < R; r += m.kstep) {
+    const int slot = ring_slot(p.head, r, C);
+    const bool in = fused && r >= p.h;
+    const f32x4 x = ld4(in ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck : s.rk + slot * DK + 4 * m.ck);
+    st4(sm + lds.k + r * lds.dks + 4 * m.ck, x);
+    if (in) st4(wk + slot * DK + 4 * m.ck, x);
+  }
+  for (int r = m.rv0 + kRecV * 16; r < R; r += 16) {
+    const int slot = ring_slot(p.head, r, C);
+    const bool in = fused && r >= p.h;
+    const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv : s.rv + slot * dv + 4 * m.cv);
+    st4(sm + lds.v + r * lds.dvs + 4 * m.cv, x);
+    if (in && !GDN) st4(wv + slot * dv + 4 * m.cv, x);
+  }
   for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
     st4(sm + lds.q + i * DK + 4 * m.ck, ld4(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
   for (int r = tid + nthr; r < R; r += nthr) {
-    sm[lds.alpha + r] = a.ring_alpha[bh * C + ring_slot(p.head, r, C)];
-    if (KIND == REPLAYSSM_GDN && r >= p.h) sm[lds.beta + (r - p.h)] = a.ring_beta[bh * C + ring_slot(p.head, r, C)];
+    const int slot = ring_slot(p.head, r, C);
+    const bool in = fused && r >= p.h;
+    const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
+    sm[lds.alpha + r] = al;
+    if (in) a.ring_alpha[s.bhC + slot] = al;
+    if (GDN && r >= p.h) {
+      const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
+      sm[lds.beta + (r - p.h)] = be;
+      if (in) a.ring_beta[s.bhC + slot] = be;
+    }
   }
 #pragma unroll
   for (int j = 0; j < kRecK; ++j) {
     const int r = m.rk0 + j * m.kstep;
-    if (r < R) st4(sm + lds.k + r * lds.dks + 4 * m.ck, rr.kb[j]);
+    if (r < R) {
+      st4(sm + lds.k + r * lds.dks + 4 * m.ck, rr.kb[j]);
+      if (fused && r >= p.h) st4(wk + ring_slot(p.head, r, C) * DK + 4 * m.ck, rr.kb[j]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
     const int r = m.rv0 + j * 16;
-    if (r < R) st4(sm + lds.v + r * lds.dvs + 4 * m.cv, rr.vb[j]);
+    if (r < R) {
+      st4(sm + lds.v + r * lds.dvs + 4 * m.cv, rr.vb[j]);
+      if (!GDN && fused && r >= p.h) st4(wv + ring_slot(p.head, r, C) * dv + 4 * m.cv, rr.vb[j]);
+    }
   }
   if (m.rk0 < T) st4(sm + lds.q + m.rk0 * DK + 4 * m.ck, rr.qv);
   for (int i = (m.rk0 < T ? m.rk0 + m.kstep : m.rk0); i < TMAX; i += m.kstep)
     if (i >= T) st4(sm + lds.q + i * DK + 4 * m.ck, f32x4{0.f, 0.f, 0.f, 0.f});  // rows of absent drafts
-  if (tid < R) sm[lds.alpha + tid] = rr.al;
-  if (KIND == REPLAYSSM_GDN && tid >= p.h && tid < R) sm[lds.beta + (tid - p.h)] = rr.be;
+  if (tid < R) {
+    sm[lds.alpha + tid] = rr.al;
+    if (fused && tid >= p.h) a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)] = rr.al;
+    if (GDN && tid >= p.h) {
+      sm[lds.beta + (tid - p.h)] = rr.be;
+      if (fused) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
+    }
+  }
 }
 
 // One item. On entry S holds its early checkpoint copy (decode/verify;
@@ -186,7 +257,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
 // item). On return rr holds (or is loading) the rows of `next` and S the
 // checkpoint of `after_next`, the item after that. Ends with a workgroup
 // barrier after its last LDS read.
-template <int KIND, int NT, int TMAX>
+template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const int item, const SeqPtr ptr,
                                             const Route rt, f32x4 (&S)[NT], RecRegs& rr, const int next,
                                             const SeqPtr nptr, const Route nrt, const int after_next) {
@@ -219,7 +290,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int64_t hoff = bh * (int64_t)(dv * DK);
 
   // The pointers were read before this item started (in the workgroup's
-  // batch read); this kernel never writes them.
+  // batch read); they are written only after every workgroup is done.
   const int head = ptr.head;
   const int hc = ptr.h;
   const int T = rt.T;
@@ -234,12 +305,12 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       load_lp<NT>(a.lp + hoff, wave, lane, S);
     }
   }
-  if (work) store_records<KIND, NT, TMAX>(a, sm, lds, item, ptr, rt, tid, nthr, map, rr);
+  if (work) store_records<KIND, NT, TMAX, FUSED>(a, sm, lds, item, ptr, rt, tid, nthr, map, rr);
   __syncthreads();
 
   // ---- the next item's ring rows: requested now, waited for by the next item
   const bool more = next < a.B * a.H;
-  if (more) load_records<KIND, NT>(a, next, nptr, nrt, tid, map, rr);
+  if (more) load_records<KIND, NT, FUSED>(a, next, nptr, nrt, tid, map, rr);
 
   // ---- matvecs y_i = S q_i (and S k_i for GDN), lane-partial over its columns.
   // A replay item does them right away, which frees S for the checkpoint two
@@ -469,23 +540,55 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 // workgroups as fit and none pays a launch per head; consecutive items of the
 // grid are neighbours in memory, so the stream over the checkpoints stays
 // sequential.
+// Advances every sequence's pointers once all items of the launch are done,
+// with the same route rule each item applied to the same (old) values: a fold
+// moves head past the folded records and adds them to `folded`; decode then
+// commits its token (h += 1, p = 0); a fused verify leaves its T drafts
+// pending (p = T). Sequences whose items were skipped set their error bit and
+// keep their pointers. Run by the last workgroup of the grid to finish (see
+// replay_kernel), all its threads striding over the sequences.
+__device__ __forceinline__ void commit_pointers(const ReplayArgs& a, int tid, int nthr) {
+  for (int b = tid; b < a.B; b += nthr) {
+    const SeqPtr p{a.head[b], a.h[b], a.p[b]};
+    const Route rt = route_of(a, p);
+    if (rt.bad) {
+      atomicOr(a.err, rt.corrupt ? REPLAYSSM_DEVERR_CORRUPT : REPLAYSSM_DEVERR_PENDING);
+      continue;
+    }
+    int head = p.head, h = p.h;
+    if (rt.fold) {
+      head += h;
+      if (head >= a.C) head -= a.C;
+      a.folded[b] += h;
+      h = 0;
+    }
+    if (a.mode == kModeDecode) {
+      h += 1;
+      a.p[b] = 0;
+    } else if (a.mode == kModeVerify && a.fused) {
+      a.p[b] = rt.T;
+    }
+    a.head[b] = head;
+    a.h[b] = h;
+  }
+}
+
 // Checkpoint prefetch depth (1: the next item's; 2: also the one after, in a
 // second register buffer). Two buffers keep more bytes in flight per
 // workgroup but cost registers, hence occupancy.
-template <int KIND, int NT, int TMAX>
+template <int KIND, int NT, int TMAX, bool FUSED>
 constexpr int prefetch_depth() {
   return REPLAYSSM_PREFETCH_DEPTH;
 }
 
-template <int KIND, int NT, int TMAX>
+template <int KIND, int NT, int TMAX, bool FUSED>
 __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
-  constexpr int DEPTH = prefetch_depth<KIND, NT, TMAX>();
+  constexpr int DEPTH = prefetch_depth<KIND, NT, TMAX, FUSED>();
   extern __shared__ f32x4 smem_v4[];
   float* sm = reinterpret_cast<float*>(smem_v4);
   const int items = a.B * a.H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = gridDim.x;
-  if ((int)blockIdx.x >= items) return;
   // Pointers of the workgroup's items are read 64 at a time, one item per
   // lane, and handed to each item with readlane: no memory round trip per item.
   int ph = 0, phc = 0, pp = 0;
@@ -502,9 +605,10 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
     return SeqPtr{__builtin_amdgcn_readlane(ph, kl), __builtin_amdgcn_readlane(phc, kl),
                   __builtin_amdgcn_readlane(pp, kl)};
   };
-  batch(blockIdx.x);
+  batch(blockIdx.x);  // (a workgroup without items still arrives at the end)
   SeqPtr ptr = ptr_at(0);
   Route rt = route_of(a, ptr);
+  if ((int)blockIdx.x >= items) rt.work = false;
   // With two checkpoint buffers they are used alternately (the loop body is
   // unrolled by two so that each has fixed registers): while one item
   // computes, the next item's checkpoint and the one after it are in flight.
@@ -518,9 +622,9 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   RecRegs rr;
   {
     const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
-    load_records<KIND, NT>(a, blockIdx.x, ptr, rt, threadIdx.x, map, rr);
+    load_records<KIND, NT, FUSED>(a, blockIdx.x, ptr, rt, threadIdx.x, map, rr);
   }
-  if (a.mode != kModeFlush) {
+  if (a.mode != kModeFlush && (int)blockIdx.x < items) {
     load_ckpt_early<NT>(a, blockIdx.x, wave, lane, SA);
     if constexpr (DEPTH == 2)
       if ((int)blockIdx.x + G < items) load_ckpt_early<NT>(a, blockIdx.x + G, wave, lane, SB);
@@ -531,7 +635,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
     if (kn == 0 && next < items) batch(next);
     const SeqPtr nptr = ptr_at(kn);
     const Route nrt = route_of(a, nptr);
-    replay_item<KIND, NT, TMAX>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt, DEPTH == 2 ? next + G : next);
+    replay_item<KIND, NT, TMAX, FUSED>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt, DEPTH == 2 ? next + G : next);
     ptr = nptr;
     rt = nrt;
   };
@@ -544,63 +648,43 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   } else {
     for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) step(k, item, SA);
   }
+
+  // Pointer commit. Each workgroup arrives once, after its last item (all its
+  // pointer reads are behind it); the last one to arrive applies the rule to
+  // every sequence. Nothing is published through the counter, so no fence is
+  // needed (see arrive_last); the new pointers reach the next kernel at the
+  // kernel boundary. One relaxed atomic per workgroup and launch, at its end.
+  int* flag = reinterpret_cast<int*>(sm);
+  if (threadIdx.x == 0) flag[0] = arrive_last(a.arrive, 0, G) ? 1 : 0;
+  __syncthreads();
+  if (flag[0]) commit_pointers(a, threadIdx.x, blockDim.x);
 }
 
-// Advances every sequence's pointers after a decode / verify / flush launch,
-// with the same route rule the replay kernel applied to the same (old) values:
-// a fold moves head past the folded records and adds them to `folded`; decode
-// then commits its token (h += 1, p = 0). Sequences the replay kernel skipped
-// set their error bit and keep their pointers. One thread per sequence; a
-// separate launch, so that the replay kernel never writes what its other
-// workgroups read (a per-sequence arrival counter instead costs far more: its
-// atomics serialise on one address per sequence).
-__global__ void __launch_bounds__(256) commit_kernel(const ReplayArgs a) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= a.B) return;
-  const SeqPtr p{a.head[b], a.h[b], a.p[b]};
-  const Route rt = route_of(a, p);
-  if (rt.bad) {
-    atomicOr(a.err, rt.corrupt ? REPLAYSSM_DEVERR_CORRUPT : REPLAYSSM_DEVERR_PENDING);
-    return;
-  }
-  int head = p.head, h = p.h;
-  if (rt.fold) {
-    head += h;
-    if (head >= a.C) head -= a.C;
-    a.folded[b] += h;
-    h = 0;
-  }
-  if (a.mode == kModeDecode) {
-    h += 1;
-    a.p[b] = 0;
-  }
-  a.head[b] = head;
-  a.h[b] = h;
-}
-
-template <int KIND, int NT, int TMAX>
+template <int KIND, int NT, int TMAX, bool FUSED>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
   const ReplayLds lds(a.C, NT * 16, a.dv, TMAX);
   const int block = a.dv / 16 * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX>), block,
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED>), block,
                                  smem, a.B * a.H, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX>), dim3((unsigned)grid), dim3((unsigned)block), smem, s,
-                     a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED>), dim3((unsigned)grid), dim3((unsigned)block), smem,
+                     s, a);
   return hipGetLastError();
+}
+
+template <int KIND, int NT, int TMAX>
+static hipError_t launch_f(const ReplayArgs& a, hipStream_t s) {
+  return a.fused ? launch_t<KIND, NT, TMAX, true>(a, s) : launch_t<KIND, NT, TMAX, false>(a, s);
 }
 
 template <int KIND, int NT>
 static hipError_t launch_nt(int tmax, const ReplayArgs& a, hipStream_t s) {
   switch (tmax) {
-    case 1: return launch_t<KIND, NT, 1>(a, s);
-    case 4: return launch_t<KIND, NT, 4>(a, s);
-    case 8: return launch_t<KIND, NT, 8>(a, s);
+    case 1: return launch_f<KIND, NT, 1>(a, s);
+    case 4: return launch_f<KIND, NT, 4>(a, s);
+    case 8: return launch_f<KIND, NT, 8>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -124,7 +124,47 @@ class Runner:
         if self.check_ring:
             self._check_ring(x, slots, T)
 
-    def _check_ring(self, x, slots, T) -> None:
+    def step(self, x: Dict[str, torch.Tensor]) -> np.ndarray:
+        """Fused append + decode (replayssm_decode_step); the oracle does append + decode."""
+        sh = self.shape
+        beta = x.get("beta")
+        out = torch.empty((sh.B, 1, sh.H, sh.P), dtype=torch.float32, device="cuda")
+        rs.decode_step(self.cfg, self.layer.struct, x["alpha"], x["k"], x["v"], beta, x["q"], out)
+        slots = self.oracle.append(self._sel(x["alpha"]), self._sel(x["k"]), self._sel(x["v"]),
+                                   None if beta is None else self._sel(beta))
+        self._slots = slots
+        if self.check_ring:
+            self._check_ring(x, slots, 1, check_v=beta is None)
+        ref, u, folds = self.oracle.decode(self._sel(x["q"]))
+        got = self._sel(out)
+        self._score(got, ref)
+        self.report.calls += 1
+        self.report.folds += sum(folds)
+        if u is not None:
+            self._check_u(u, 1)
+        return got
+
+    def verify_step(self, x: Dict[str, torch.Tensor], T: int) -> np.ndarray:
+        """Fused append + verify (replayssm_verify_step)."""
+        sh = self.shape
+        beta = x.get("beta")
+        out = torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda")
+        rs.verify_step(self.cfg, self.layer.struct, T, x["alpha"], x["k"], x["v"], beta, x["q"], out)
+        slots = self.oracle.append(self._sel(x["alpha"]), self._sel(x["k"]), self._sel(x["v"]),
+                                   None if beta is None else self._sel(beta))
+        self._slots = slots
+        if self.check_ring:
+            self._check_ring(x, slots, T, check_v=beta is None)
+        ref, u, folds = self.oracle.verify(self._sel(x["q"]))
+        got = self._sel(out)
+        self._score(got, ref)
+        self.report.calls += 1
+        self.report.folds += sum(folds)
+        if u is not None:
+            self._check_u(u, T)
+        return got
+
+    def _check_ring(self, x, slots, T, check_v=True) -> None:
         # committed-record copies are bit-exact copies of the inputs (k and alpha always, v for Mamba-2
         # until the record is consumed, where GDN replaces it by u)
         sl = torch.tensor([[slots[b][i] for i in range(T)] for b, _ in self.heads], device="cuda")
@@ -133,7 +173,8 @@ class Runner:
             ring_a = self.layer.ring_alpha[self.bs, self.hs, sl[:, i]]
             ring_v = self.layer.ring_v[self.bs, self.hs, sl[:, i]]
             ok = torch.equal(ring_k, x["k"][self.bs, i, self.hs]) and torch.equal(ring_a, x["alpha"][self.bs, i, self.hs])
-            ok = ok and torch.equal(ring_v, x["v"][self.bs, i, self.hs])
+            if check_v:
+                ok = ok and torch.equal(ring_v, x["v"][self.bs, i, self.hs])
             if "beta" in x:
                 ok = ok and torch.equal(self.layer.ring_beta[self.bs, self.hs, sl[:, i]], x["beta"][self.bs, i, self.hs])
             if not ok:
@@ -210,11 +251,14 @@ class Runner:
         return self.report.err_word
 
 
-def run_standard(runner: Runner, steps: int, check_every: int = 1) -> Report:
+def run_standard(runner: Runner, steps: int, check_every: int = 1, fused: bool = False) -> Report:
     for t in range(steps):
         x = runner.inputs(1)
-        runner.append(x, 1)
-        runner.decode(x)
+        if fused:
+            runner.step(x)
+        else:
+            runner.append(x, 1)
+            runner.decode(x)
         if (t + 1) % check_every == 0 or t == steps - 1:
             runner.check_pointers()
     runner.check_checkpoint("hp" if runner.cfg.precision != rs.BF16_SHARED else "lp")
@@ -223,12 +267,16 @@ def run_standard(runner: Runner, steps: int, check_every: int = 1) -> Report:
     return runner.report
 
 
-def run_spec(runner: Runner, T: int, rounds: int, check_every: int = 1, accept_mode: str = "uniform") -> Report:
+def run_spec(runner: Runner, T: int, rounds: int, check_every: int = 1, accept_mode: str = "uniform",
+             fused: bool = False) -> Report:
     sh = runner.shape
     for rnd in range(rounds):
         x = runner.inputs(T)
-        runner.append(x, T)
-        runner.verify(x, T)
+        if fused:
+            runner.verify_step(x, T)
+        else:
+            runner.append(x, T)
+            runner.verify(x, T)
         if accept_mode == "all":
             a = torch.full((sh.B,), T, dtype=torch.int32, device="cuda")
         elif runner.gen == "host":

@@ -39,6 +39,16 @@ def test_mamba2_decode_b256_512_steps():
     assert rep.final_pointers["head"] == [3] * sh.B
 
 
+def test_mamba2_decode_step_b256_512_steps():
+    """The fused append + decode launch the benchmark times, at full size."""
+    w = WORKLOADS["mamba2_decode_b256"]
+    sh = w.shape
+    r = Runner(sh, w.L, 1, wid=w.wid + 200, heads=sample_heads(sh.B, sh.H, 48), gen="device", s0_sigma=w.s0_sigma)
+    rep = run_standard(r, w.steps, check_every=16, fused=True)
+    _clean(rep)
+    assert rep.final_pointers["folded"] == [496] * sh.B and rep.final_pointers["h"] == [16] * sh.B
+
+
 def test_mamba2_spec_b256_256_rounds():
     """Same layer, T=4 drafts, C=20, accepted prefix uniform in 0..4, 256 rounds."""
     w = WORKLOADS["mamba2_spec_b256"]

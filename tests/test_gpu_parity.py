@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import ssm_decode_amd as rs
-from synth import LayerShape, WORKLOADS
+from synth import LayerShape, WORKLOADS, host_initial_state, host_step
 
 from harness import Runner, run_spec, run_standard, sample_heads
 
@@ -117,3 +117,43 @@ def test_wide_window_spec(kind):
     r = Runner(sh, 56, 8, wid=61, decay="slow")
     rep = run_spec(r, 8, 24)
     _assert_clean(rep)
+
+
+@pytest.mark.parametrize("kind,P,N,L", [("mamba2", 64, 128, 16), ("mamba2", 16, 16, 4), ("gdn", 128, 128, 5),
+                                        ("gdn", 32, 64, 64)])
+def test_fused_decode_step(kind, P, N, L):
+    """replayssm_decode_step = append + decode in one launch: same oracle bar, ring written by it."""
+    sh = LayerShape(kind, 3, 5, P, N)
+    r = Runner(sh, L, 1, wid=110, decay="slow")
+    rep = run_standard(r, 2 * L + 7, fused=True)
+    _assert_clean(rep)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("T,L", [(4, 16), (3, 5), (8, 8)])
+def test_fused_verify_step(kind, T, L):
+    sh = LayerShape(kind, 4, 3, 64, 128)
+    r = Runner(sh, L, T, wid=111 + T)
+    rep = run_spec(r, T, 30, fused=True)
+    _assert_clean(rep)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_fused_equals_unfused_bitwise(kind):
+    """Same inputs through append+decode and through decode_step: identical bits everywhere."""
+    sh = LayerShape(kind, 5, 4, 64, 128)
+    S0 = torch.from_numpy(host_initial_state(0, 112, sh, 0.1)).cuda()
+    cfg = rs.make_config(kind, "fp32", sh.B, sh.H, sh.P, sh.N, 6, 1)
+    la, lb = rs.LayerState(cfg), rs.LayerState(cfg)
+    la.import_state(S0)
+    lb.import_state(S0)
+    oa = torch.empty((sh.B, sh.H, sh.P), device="cuda")
+    ob = torch.empty_like(oa)
+    for t in range(20):
+        x = {k: torch.from_numpy(v).cuda() for k, v in host_step(0, 112, t, sh, 1).items()}
+        rs.append(cfg, la.struct, 1, x["alpha"], x["k"], x["v"], x.get("beta"))
+        rs.decode(cfg, la.struct, x["q"], oa)
+        rs.decode_step(cfg, lb.struct, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], ob)
+        assert torch.equal(oa, ob), t
+    assert torch.equal(la.hp, lb.hp) and torch.equal(la.ring_k, lb.ring_k) and torch.equal(la.ring_v, lb.ring_v)
+    assert torch.equal(la.ring_alpha, lb.ring_alpha) and la.pointers() == lb.pointers()
