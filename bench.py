@@ -19,9 +19,15 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
              8 TB/s
   unfused    the same step as replayssm_append + replayssm_decode
   eager      the conventional kernel that loads and stores the state every step
-  workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint
+  workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint;
+             with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
+             each warm (one layer) and rotated (rounds cycle over layer instances
+             holding >= 2 GiB of state, so the on-package cache cannot hold it)
+  ceilings   practical HBM ceilings measured on the device: a read-only probe in
+             the checkpoint stream's access pattern, and a device-to-device copy
   cpu_baseline  the CPU oracle (fp64 eager recurrence, OpenMP over heads) on a
-             bounded sample of the same workload, scaled to tokens/s
+             bounded sample of the same workload, scaled to tokens/s; also on one
+             core and on the Gated DeltaNet workload
 """
 from __future__ import annotations
 
@@ -38,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSM-layer decode tokens/sec at B=256 (+ achieved HBM GB/s vs MI355X peak)"
 HBM_PEAK_GBS = 8000.0
+MFMA_F32_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak of MI355X
 POOL_BYTES_MAX = 8 << 30
 
 
@@ -236,25 +243,36 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
     return res
 
 
-def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, kernel_pass=True, fused=True):
+def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, kernel_pass=True, fused=True,
+             rotate_bytes=0):
+    """Speculative rounds (verify T drafts, then accept). With rotate_bytes > 0 the rounds cycle over
+    enough independent layer instances to hold that many bytes of state, as the layers of a model
+    do, so that consecutive rounds do not find their state in the on-package cache."""
     sh = w.shape
     if B is not None:
         sh = synth.LayerShape(sh.kind, B, sh.H, sh.P, sh.N)
     prec = precision or w.precision
     T = w.T if w.T > 1 else int(w.extra.get("spec_T", 4))
     cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, T)
-    layer = rs.LayerState(cfg)
-    layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
+    S0 = synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda")
+    lays = [rs.LayerState(cfg)]
+    footprint = sum(t.numel() * t.element_size() for t in lays[0].tensors())
+    layers = max(1, -(-int(rotate_bytes) // footprint))
+    lays += [rs.LayerState(cfg) for _ in range(layers - 1)]
+    for lay in lays:
+        lay.import_state(S0)
+    del S0
     rb = record_bytes(sh.kind, sh.P, sh.N)
     n = warmup + 2 * rounds  # both timed passes get their own acceptance draws
     pool = make_pool(torch, synth, sh, T, n, seed, w.wid, sh.B * sh.H * T * (rb + 4 * (sh.N + sh.P)))
     accs = [synth.device_accept(seed, w.wid, r, sh.B, T, "cuda") for r in range(n)]
     acc_host = [a.cpu().numpy() for a in accs]
     out = torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda")
-    st, stream = layer.struct, torch.cuda.current_stream()
+    stream = torch.cuda.current_stream()
 
     def rnd(i, evs=None):
         x = pool[i % len(pool)]
+        st = lays[i % layers].struct
         if not fused:
             rs.append(cfg, st, T, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
         if evs is not None:
@@ -267,30 +285,34 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
             evs[1].record(stream)
         rs.accept(cfg, st, accs[i], stream)
 
-    for i in range(warmup):
-        rnd(i)
-    torch.cuda.synchronize()
-    hs = layer.h.cpu().numpy().astype(np.int64)
-    with Timer(torch) as tm:
-        for i in range(rounds):
-            rnd(warmup + i)
-    accepted = int(sum(acc_host[warmup + i].sum() for i in range(rounds)))
-    # per-sequence byte count from the pointer rule
-    kb = 0
-    h = hs.copy()
-    for i in range(rounds):
+    def launch_bytes(h, first):
+        """Algorithmic bytes of rounds first.. with per-layer h arrays advanced in place."""
         fold = h + T > w.L
+        kb = 0
         for f in (False, True):
             m = fold == f
             if m.any():
                 kb += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f, fused) for hh in h[m]) * sh.H
-        h = np.where(fold, 0, h) + acc_host[warmup + i]
+        return kb, np.where(fold, 0, h) + acc_host[first]
+
+    for i in range(warmup):
+        rnd(i)
+    torch.cuda.synchronize()
+    hs = [lay.h.cpu().numpy().astype(np.int64) for lay in lays]
+    with Timer(torch) as tm:
+        for i in range(rounds):
+            rnd(warmup + i)
+    accepted = int(sum(acc_host[warmup + i].sum() for i in range(rounds)))
+    kb = 0
+    for i in range(rounds):
+        b, hs[(warmup + i) % layers] = launch_bytes(hs[(warmup + i) % layers], warmup + i)
+        kb += b
     res = {"ms": tm.ms, "rounds": rounds, "accepted_tokens": accepted, "drafts": sh.B * T * rounds,
-           "verify_bytes": int(kb)}
+           "verify_bytes": int(kb), "layers": layers, "layer_footprint_MiB": footprint / 2**20}
     if kernel_pass:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
-        h = layer.h.cpu().numpy().astype(np.int64)
         torch.cuda.synchronize()
+        hs = [lay.h.cpu().numpy().astype(np.int64) for lay in lays]
         base = warmup + rounds
         for i in range(rounds):
             rnd(base + i, evs[i])
@@ -298,16 +320,13 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
         durs = np.array([a.elapsed_time(b) for a, b in evs])
         kb2 = 0
         for i in range(rounds):
-            fold = h + T > w.L
-            for f in (False, True):
-                m = fold == f
-                if m.any():
-                    kb2 += sum(replay_launch_bytes(sh.kind, prec, sh.P, sh.N, int(hh), T, f, fused) for hh in h[m]) * sh.H
-            h = np.where(fold, 0, h) + acc_host[base + i]
+            b, hs[(base + i) % layers] = launch_bytes(hs[(base + i) % layers], base + i)
+            kb2 += b
         res.update({"kernel_avg_us": float(durs.mean() * 1e3), "kernel_gbs": kb2 / (durs.sum() * 1e6)})
-    err = rs.read_error(st)
-    if err:
-        raise RuntimeError(f"device error word {err}")
+    for lay in lays:
+        err = rs.read_error(lay.struct)
+        if err:
+            raise RuntimeError(f"device error word {err}")
     return res
 
 
@@ -345,9 +364,46 @@ def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
     return {"ms": tm.ms, "steps": steps, "tokens": sh.B * T * steps, "bytes": b, "gbs": b / (tm.ms * 1e6)}
 
 
-def cpu_baseline(synth, w, seed, seconds):
+def ceilings(torch, rs):
+    """Practical HBM ceilings of the device: the read probe (the decode kernel's checkpoint access
+    pattern, read-only) over 4 GiB, and a 2 GiB device-to-device copy (2 bytes moved per byte)."""
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        rs.probe_read(src, sink, stream)
+    reps = 20
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            rs.probe_read(src, sink, stream)
+    read = src.numel() * 4 * reps / (tm.ms * 1e6)
+    a = src[: 1 << 29]
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    with Timer(torch) as tm:
+        for _ in range(reps):
+            b.copy_(a)
+    copy = 2 * a.numel() * 4 * reps / (tm.ms * 1e6)
+    del src, a, b
+    torch.cuda.empty_cache()
+    return {"read_probe_gbs": read, "d2d_copy_gbs": copy, "unit": "GB/s",
+            "read_probe": "replayssm_probe_read over 4 GiB (persistent workgroups, 32 KiB per pass, "
+                          "non-temporal 16-byte loads)", "d2d_copy": "torch copy_ of 2 GiB (hipMemcpy D2D)"}
+
+
+def cpu_baseline(synth, w, seed, seconds, threads=None):
     """The oracle as it stands, on a bounded sample of the workload: B' sequences (all heads)."""
     import oracle
+
+    if threads is not None:
+        prev = oracle.num_threads()
+        oracle.set_num_threads(threads)
+        try:
+            return cpu_baseline(synth, w, seed, seconds)
+        finally:
+            oracle.set_num_threads(prev)
 
     sh = w.shape
     Bs = 64
@@ -393,6 +449,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     sh = w.shape
     main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed)
+    fold_flops = 2 * sh.P * sh.N * w.L * sh.B * sh.H  # V diag(gamma) K^T over the L folded records
     tok_s = main_res["tokens"] / (main_res["ms"] * 1e-3)
     achieved = main_res["kernel_bytes"] / (main_res["kernel_ms_total"] * 1e6)
     line = {
@@ -417,7 +474,11 @@ def main():
                      "algorithmic_bytes_per_launch": main_res["kernel_bytes"] / main_res["kernel_launches"],
                      "plain_step_us": main_res["plain_avg_us"], "fold_step_us": main_res["fold_avg_us"],
                      "plain_step_gbs": main_res["plain_gbs"], "fold_step_gbs": main_res["fold_gbs"],
-                     "us_by_h_before_step": main_res["us_by_h"]},
+                     "us_by_h_before_step": main_res["us_by_h"],
+                     "fold_mfma": None if not main_res["fold_avg_us"] else {
+                         "tflops": fold_flops / (main_res["fold_avg_us"] * 1e6), "peak": MFMA_F32_PEAK_TFLOPS,
+                         "frac": fold_flops / (main_res["fold_avg_us"] * 1e6) / MFMA_F32_PEAK_TFLOPS,
+                         "flops_per_fold_step": fold_flops}},
         "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
         "step": "replayssm_decode_step (append + decode in one launch)",
     }
@@ -457,14 +518,27 @@ def main():
             r4[prec] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
                         "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"]}
         if args.sweep:
-            for B in (1, 32, 512):
-                r = run_spec(torch, rs, synth, w4, 64, 8, args.seed, B=B)
-                r4[f"fp32_hp_bf16_lp_B{B}"] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
-                                               "verify_kernel_gbs": r["kernel_gbs"]}
+            sweep = {}
+            for B in (1, 32, 256, 512):
+                for label, rot in (("warm", 0), ("rotated", 2 << 30)):
+                    r = run_spec(torch, rs, synth, w4, 128, 16, args.seed, B=B, rotate_bytes=rot)
+                    sweep[f"B{B}_{label}"] = {
+                        "accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
+                        "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"],
+                        "layers": r["layers"], "layer_footprint_MiB": round(r["layer_footprint_MiB"], 1)}
+            r4["batch_sweep_fp32_hp_bf16_lp"] = sweep
         wl[w4.name] = r4
+        line["ceilings"] = ceilings(torch, rs)
         line["workloads"] = wl
     if not (args.quick or args.no_cpu_baseline):
         line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds)
+        if not args.quick:
+            one = cpu_baseline(synth, w, args.seed, args.cpu_seconds / 2, threads=1)
+            g = synth.WORKLOADS["gdn_decode_b256"]
+            gd = cpu_baseline(synth, g, args.seed, args.cpu_seconds / 2)
+            line["cpu_baseline"]["more"] = {
+                "one_core": {"value": one["value"], "cores": one["cores"], "sample": one["sample"]},
+                g.name: {"value": gd["value"], "cores": gd["cores"], "sample": gd["sample"]}}
     print(json.dumps(line), flush=True)
 
 

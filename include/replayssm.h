@@ -263,6 +263,16 @@ int replayssm_eager_verify(const replayssm_config* cfg, float* pool, const int32
 int replayssm_eager_accept(const replayssm_config* cfg, int32_t* slot, const int32_t* accepted,
                            int T, void* stream);
 
+/* ---- Measurement helper (not a step of the method) -------------------------------------
+ * Reads `bytes` bytes at device address `src` once, in the access pattern of the replay
+ * kernel's checkpoint stream (persistent workgroups, 32 KiB per workgroup per pass, 16-byte
+ * non-temporal loads), and discards them. Timing it gives the practical HBM read ceiling
+ * the decode kernel's bandwidth is set beside. `src` must be 16-byte aligned and `bytes` a
+ * positive multiple of 16; `sink` is a device float that is written only in the
+ * (practically impossible) case that the loaded values sum to one specific NaN pattern.
+ * Enqueued on `stream`; EINVAL on bad arguments, EHIP on a launch failure. */
+int replayssm_probe_read(const void* src, int64_t bytes, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,7 @@ def lib():
         L.oracle_gdn_round_f64.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_gdn_round_f32.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -57,6 +58,10 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
 
 
 def mamba2_round(S, alpha, k, v, q, acc, precision: str = "f64"):

@@ -204,3 +204,6 @@ int oracle_num_threads(void) {
   }
   return n;
 }
+
+/* Sets the thread count of the following oracle calls (the CPU baseline runs at one core too). */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -76,6 +76,7 @@ SIGNATURES = {
     "replayssm_eager_step": [ctypes.POINTER(Config), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "replayssm_eager_verify": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "replayssm_eager_accept": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp],
+    "replayssm_probe_read": [_vp, ctypes.c_int64, _vp, _vp],
 }
 STRING_FUNCTIONS = {"replayssm_status_string": [ctypes.c_int], "replayssm_last_error": []}
 
@@ -218,6 +219,12 @@ def eager_accept(cfg, slot, accepted, T, stream=None):
            "eager_accept")
 
 
+def probe_read(src, sink, stream=None):
+    """Enqueue one pass of the read-ceiling probe over `src` (a CUDA tensor); `sink` is one float32."""
+    _check(lib().replayssm_probe_read(_p(src), ctypes.c_int64(src.numel() * src.element_size()), _f32(sink),
+                                      _s(stream)), "probe_read")
+
+
 class LayerState:
     """Device memory (torch tensors) for one layer's ReplaySSM state, plus the C struct.
 
@@ -261,6 +268,11 @@ class LayerState:
         else:
             unpack_state(cfg, None, self.lp, dst, stream)
         return dst
+
+    def tensors(self):
+        """Every device tensor the layer's state holds."""
+        return [t for t in (self.hp, self.lp, self.ring_alpha, self.ring_beta, self.ring_k, self.ring_v, self.head,
+                            self.h, self.p, self.folded, self.arrive, self.err) if t is not None]
 
     def pointers(self):
         return {"head": self.head.tolist(), "h": self.h.tolist(), "p": self.p.tolist(),

@@ -386,4 +386,12 @@ int replayssm_eager_accept(const replayssm_config* cfg, int32_t* slot, const int
                     "eager_accept");
 }
 
+int replayssm_probe_read(const void* src, int64_t bytes, float* sink, void* stream) {
+  NEED(src);
+  if (sink == nullptr) return fail(REPLAYSSM_EINVAL, "sink is NULL");
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(REPLAYSSM_EINVAL, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  return hip_result(rs::launch_probe_read(src, bytes, sink, as_stream(stream)), "probe_read");
+}
+
 }  // extern "C"

@@ -135,5 +135,6 @@ hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_
                          int dk, hipStream_t s);
 hipError_t launch_eager(int kind, int dk, const EagerArgs& a, hipStream_t s);
 hipError_t launch_eager_accept(int32_t* slot, const int32_t* acc, int B, int T, hipStream_t s);
+hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 
 }  // namespace rs

@@ -107,6 +107,11 @@ def test_calls_reject_bad_arguments_before_enqueueing(rs):
     assert L.replayssm_pack_state(ctypes.byref(cfg), fake, None, None, None) == rs.EINVAL
     assert L.replayssm_unpack_state(ctypes.byref(cfg), None, None, fake, None) == rs.EINVAL
     assert L.replayssm_read_error(None, None, None) == rs.EINVAL
+    assert L.replayssm_probe_read(None, 1024, fake, None) == rs.EINVAL
+    assert L.replayssm_probe_read(fake, 1000, fake, None) == rs.EINVAL
+    assert "multiple of 16" in rs.last_error()
+    assert L.replayssm_probe_read(fake, 0, fake, None) == rs.EINVAL
+    assert L.replayssm_probe_read(fake, 1024, None, None) == rs.EINVAL
 
 
 def test_status_strings(rs):
