@@ -71,6 +71,20 @@ __device__ __forceinline__ void load_lp(const uint16_t* head_base, int wave, int
   }
 }
 
+// The raw 16-byte chunks of the bf16 copy land in S[0 .. NT/2) as loaded;
+// widen_lp turns them into the lane's fp32 tiles in place. Keeping the loaded
+// bits untouched until the values are needed lets the load stay in flight.
+template <int NT>
+__device__ __forceinline__ void widen_lp(f32x4 (&S)[NT]) {
+  static_assert(NT % 2 == 0, "the bf16 layout pairs tiles");
+  // highest chunk first: chunk m fills tiles 2m and 2m + 1, which hold no chunk still to be read
+#pragma unroll
+  for (int m = NT / 2 - 1; m >= 0; --m) {
+    const u32x4 w = __builtin_bit_cast(u32x4, S[m]);
+    unpack_lp_chunk(uint4{w[0], w[1], w[2], w[3]}, S[2 * m], S[2 * m + 1]);
+  }
+}
+
 // fp32 registers -> bf16 copy (round to nearest even); returns the rounded values in S when asked.
 template <int NT>
 __device__ __forceinline__ void store_lp(uint16_t* head_base, int wave, int lane, f32x4 (&S)[NT],
@@ -107,10 +121,10 @@ __device__ __forceinline__ float sum_width(float x) {
   return x;
 }
 
-// Arrival counting for the per-sequence pointer update ("last arriver").
-// Counts the workgroups of sequence b that have read b's pointers; returns
-// true in the single thread of the last one, which may then update them: every
-// other workgroup of b read them before arriving, so nothing reads them after.
+// Arrival counting for the pointer update ("last arriver"). Counts the
+// workgroups that have read the pointers guarded by counter b; returns true in
+// the single thread of the last one, which may then update them: every other
+// workgroup read them before arriving, so nothing reads them after.
 // The caller must have synchronised its workgroup after its pointer reads. The
 // counter is reset to zero for the next launch.
 //
@@ -122,7 +136,7 @@ __device__ __forceinline__ float sum_width(float x) {
 // values become visible to the next kernel at the kernel boundary. (An
 // agent-scope fence here would write back and invalidate the XCD's L2 once
 // per workgroup, which costs more than the whole decode.) The replay kernel
-// splits the same protocol in two (atomic early, test late).
+// uses it once per workgroup, after the workgroup's last item.
 __device__ __forceinline__ bool arrive_last(int32_t* arrive, int b, int expected) {
   const int prev = atomicAdd(arrive + b, 1);
   if (prev != expected - 1) return false;

@@ -97,7 +97,7 @@ struct EagerArgs {
 // wavefront reading one column of four consecutive rows hit distinct banks.
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, gf, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
   __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
@@ -112,8 +112,7 @@ struct ReplayLds {
     gk = gq + pad4((C + 1) * tmax);
     cq = gk + pad4((C + 1) * tmax);
     ck = cq + pad4(C * tmax);
-    gf = ck + pad4(C * tmax);
-    total = gf + pad4(C + 1);
+    total = ck + pad4(C * tmax);
   }
 };
 

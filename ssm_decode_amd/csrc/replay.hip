@@ -33,14 +33,14 @@
 //
 // Pipelining: right after step 1 the workgroup requests the next item's ring
 // records (into registers), and as soon as this item's mat-vecs have consumed
-// S, the next item's checkpoint (into S). Both stream in while this item
-// computes. Vector loads complete in order, so the next item can wait for its
-// records without waiting for its checkpoint.
+// S, the next item's checkpoint (into S, in the precision that item's route
+// reads). Both stream in while this item computes. Vector memory operations
+// complete in order and the compiler waits on them by count, so every path
+// through an item issues the same loads in the same order (a load that has
+// nothing to fetch reads one fixed location instead of being skipped): the
+// next item then waits for its records without waiting for its checkpoint, and
+// for its checkpoint without waiting for the records requested after it.
 #include "device.hpp"
-
-#ifndef REPLAYSSM_PREFETCH_DEPTH
-#define REPLAYSSM_PREFETCH_DEPTH 1
-#endif
 
 namespace rs {
 
@@ -76,17 +76,33 @@ __device__ __forceinline__ Route route_of(const ReplayArgs& a, const SeqPtr& p) 
   return r;
 }
 
-// The checkpoint copy a decode/verify call reads for `item` before it knows
-// the route: fp32 in FP32 mode, the bf16 copy otherwise (a fold step of the
-// two-precision mode reloads fp32 once it knows).
+// Which checkpoint copy an item reads: the bf16 one in the shared-bf16 mode,
+// and on the non-fold steps of the two-precision mode; fp32 otherwise.
+__device__ __forceinline__ bool reads_lp(int precision, bool fold) {
+  return precision == REPLAYSSM_BF16_SHARED || (precision == REPLAYSSM_FP32_HP_BF16_LP && !fold);
+}
+
+// Requests the checkpoint copy of `item` into S: the fp32 tiles, or the bf16
+// copy's raw 16-byte chunks in S[0, NT/2) (widened in place when used). Both
+// forms are the same NT loads per lane with computed addresses, no branch: in
+// the bf16 form the loads into S[NT/2, NT) read distinct 16-byte chunks at the
+// start of the array (widening overwrites them), and with valid false (no
+// item, or an item with nothing to do) all of them read the array's first
+// bytes.
 template <int NT>
-__device__ __forceinline__ void load_ckpt_early(const ReplayArgs& a, int item, int wave, int lane,
-                                                f32x4 (&S)[NT]) {
-  const int64_t hoff = (int64_t)item * (a.dv * NT * 16);
-  if (a.precision == REPLAYSSM_FP32) {
-    load_hp<NT>(a.hp + hoff, wave, lane, S);
-  } else if constexpr (NT >= 2) {
-    load_lp<NT>(a.lp + hoff, wave, lane, S);
+__device__ __forceinline__ void prefetch_ckpt(const ReplayArgs& a, int item, bool fold, bool valid, int wave,
+                                              int lane, f32x4 (&S)[NT]) {
+  const bool lp = reads_lp(a.precision, fold);
+  const char* base = lp ? reinterpret_cast<const char*>(a.lp) : reinterpret_cast<const char*>(a.hp);
+  const int64_t head_bytes = (int64_t)a.dv * NT * 16 * (lp ? 2 : 4);
+  const int first_chunk = lp ? wave * (NT / 2) : wave * NT;  // 1 KiB chunks: 64 lanes x 16 bytes
+  const int64_t start = valid ? (int64_t)item * head_bytes + (int64_t)first_chunk * 1024 + lane * 16 : 0;
+  const int step = valid ? 1024 : 0;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bool pad = lp && nt >= NT / 2;
+    const char* src = pad ? base + nt * 16 : base + start + nt * step;
+    S[nt] = __builtin_bit_cast(f32x4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)));
   }
 }
 
@@ -149,33 +165,39 @@ __device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) 
 
 template <int KIND, int NT, bool FUSED>
 __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, const SeqPtr& p, const Route& rt,
-                                             int tid, const StageMap& m, RecRegs& rr) {
+                                             bool valid, int tid, const StageMap& m, RecRegs& rr) {
   constexpr int DK = NT * 16;
-  if (!rt.work) return;
-  const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
-  const int b = item / H, hd = item - b * H;
-  const RowSrc s = row_src<NT>(a, item, T);
+  // Every load is issued; one with nothing to fetch reads the first element of a
+  // ring array (always allocated: q and the inputs are NULL in a flush call).
+  const bool ok = valid && rt.work;
+  const int H = a.H, C = a.C, dv = a.dv, T = ok ? rt.T : 0, R = ok ? rt.R : 0;
+  const int b = ok ? item / H : 0, hd = ok ? item - b * H : 0;
+  const RowSrc s = row_src<NT>(a, ok ? item : 0, T);
   constexpr bool fused = FUSED;
 #pragma unroll
   for (int j = 0; j < kRecK; ++j) {
     const int r = m.rk0 + j * m.kstep;
-    if (r < R)
-      rr.kb[j] = ld4((fused && r >= p.h) ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck
-                                         : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck);
+    const float* src = (fused && r >= p.h) ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck
+                                           : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck;
+    rr.kb[j] = ld4(r < R ? src : a.ring_k);
   }
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
     const int r = m.rv0 + j * 16;
-    if (r < R)
-      rr.vb[j] = ld4((fused && r >= p.h) ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
-                                         : s.rv + ring_slot(p.head, r, C) * dv + 4 * m.cv);
+    const float* src = (fused && r >= p.h) ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
+                                           : s.rv + ring_slot(p.head, r, C) * dv + 4 * m.cv;
+    rr.vb[j] = ld4(r < R ? src : a.ring_v);
   }
-  if (m.rk0 < T) rr.qv = ld4(a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck);
-  if (tid < R) {
-    rr.al = (fused && tid >= p.h) ? a.in_alpha[s.ia + (int64_t)(tid - p.h) * H]
-                                  : a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)];
-    if (KIND == REPLAYSSM_GDN && tid >= p.h)
-      rr.be = fused ? a.in_beta[s.ia + (int64_t)(tid - p.h) * H] : a.ring_beta[s.bhC + ring_slot(p.head, tid, C)];
+  rr.qv = ld4(m.rk0 < T ? a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck : a.ring_k);
+  {
+    const float* src = (fused && tid >= p.h) ? a.in_alpha + s.ia + (int64_t)(tid - p.h) * H
+                                             : a.ring_alpha + s.bhC + ring_slot(p.head, tid, C);
+    rr.al = *(tid < R ? src : a.ring_alpha);
+  }
+  if (KIND == REPLAYSSM_GDN) {
+    const float* src = fused ? a.in_beta + s.ia + (int64_t)(tid - p.h) * H
+                             : a.ring_beta + s.bhC + ring_slot(p.head, tid, C);
+    rr.be = *((tid < R && tid >= p.h) ? src : a.ring_beta);
   }
 }
 
@@ -252,15 +274,14 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   }
 }
 
-// One item. On entry S holds its early checkpoint copy (decode/verify;
-// requested two items ago) and rr its ring rows (requested during the previous
-// item). On return rr holds (or is loading) the rows of `next` and S the
-// checkpoint of `after_next`, the item after that. Ends with a workgroup
-// barrier after its last LDS read.
+// One item. On entry S holds (or is loading) the checkpoint copy the item's
+// route reads, and rr its ring rows; both were requested during the previous
+// item. On return rr holds (or is loading) the rows of `next` and S its
+// checkpoint copy. Ends with a workgroup barrier after its last LDS read.
 template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const int item, const SeqPtr ptr,
                                             const Route rt, f32x4 (&S)[NT], RecRegs& rr, const int next,
-                                            const SeqPtr nptr, const Route nrt, const int after_next) {
+                                            const SeqPtr nptr, const Route nrt) {
   constexpr int DK = NT * 16;
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
   constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
@@ -297,27 +318,26 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const bool corrupt = rt.corrupt, bad = rt.bad, fold = rt.fold, work = rt.work, outputs = rt.outputs;
   const int R = rt.R, r0 = rt.r0;
 
-  // ---- 1. checkpoint and records ----------------------------------------------
-  if (fold && (mode == kModeFlush || prec == REPLAYSSM_FP32_HP_BF16_LP)) {
-    if (prec != REPLAYSSM_BF16_SHARED) {
-      load_hp<NT>(a.hp + hoff, wave, lane, S);
-    } else if constexpr (NT >= 2) {
-      load_lp<NT>(a.lp + hoff, wave, lane, S);
-    }
-  }
+  // ---- 1. records (the checkpoint copy is already in flight) --------------------
   if (work) store_records<KIND, NT, TMAX, FUSED>(a, sm, lds, item, ptr, rt, tid, nthr, map, rr);
   __syncthreads();
 
   // ---- the next item's ring rows: requested now, waited for by the next item
   const bool more = next < a.B * a.H;
-  if (more) load_records<KIND, NT, FUSED>(a, next, nptr, nrt, tid, map, rr);
+  load_records<KIND, NT, FUSED>(a, next, nptr, nrt, more, tid, map, rr);
+  // the next item's checkpoint copy, requested once S is free (same loads on every path). The
+  // empty asm marks every S register as read here, on every path: no load into S can still be
+  // pending when S is reloaded, so the compiler's waits before the reload stay at zero.
+  auto prefetch_next = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) __asm__ volatile("" ::"v"(S[nt]));
+    prefetch_ckpt<NT>(a, next, nrt.fold, more && nrt.work, wave, lane, S);
+  };
+  const bool lp = reads_lp(prec, fold);
 
   // ---- matvecs y_i = S q_i (and S k_i for GDN), lane-partial over its columns.
-  // A replay item does them right away, which frees S for the checkpoint two
-  // items ahead (the other buffer already holds the next item's). A fold item
-  // does them on the folded state, further down.
-  const bool prefetch = after_next < a.B * a.H && mode != kModeFlush;
-  if (!work && prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
+  // A replay item does them right away, which frees S for the next item's
+  // checkpoint. A fold item does them on the folded state, further down.
   float yq[TMAX], yk[TMAX];
 #pragma unroll
   for (int i = 0; i < TMAX; ++i) {
@@ -336,42 +356,23 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       }
     }
   };
-  if (outputs && !fold) {
-    matvec();
-    if (prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
-  }
 
   // ---- 2. decay products and record dot products -----------------------------
   // gq[r + 1][i] = prod of alpha over records (r, hc + i]: the decay of record r
   // at draft i; gk[r + 1][i] the same over (r, hc + i - 1]: at the state just
   // before draft i. Row r0 (r = r0 - 1) holds the checkpoint's factors Gamma_i
   // and Gamma_{i-1}. Entries of records after the end point are zero.
-  // gf[t] = prod of alpha over committed records [t, hc): gf[0] = Gamma_h
-  // scales the checkpoint in a fold, gf[j + 1] weighs record j.
   // Each product set is one suffix-product scan across a wavefront (lane l
   // stands for record first + l), one wavefront per end point.
-  if (work) {
-    const bool wide = (R - r0 + 1 > kWave) || (hc + 1 > kWave);
+  auto scans_and_dots = [&]() {
+  if (outputs) {
+    const bool wide = R - r0 + 1 > kWave;
     if (!wide) {
-      const int njobs = (outputs ? 2 * T : 0) + (fold ? 1 : 0);
-      for (int job = wave; job < njobs; job += W) {
-        int first, e, last;
-        float* out;
-        int stride;
-        if (job < 2 * T && outputs) {
-          const int i = job >> 1;
-          first = r0 - 1;
-          last = R - 1;
-          e = (job & 1) ? hc + i - 1 : hc + i;
-          out = sm + ((job & 1) ? lds.gk : lds.gq) + i;
-          stride = TMAX;
-        } else {
-          first = -1;
-          last = hc - 1;
-          e = hc - 1;
-          out = sm + lds.gf;
-          stride = 1;
-        }
+      for (int job = wave; job < 2 * T; job += W) {
+        const int i = job >> 1;
+        const int first = r0 - 1, last = R - 1;
+        const int e = (job & 1) ? hc + i - 1 : hc + i;
+        float* out = sm + ((job & 1) ? lds.gk : lds.gq) + i;
         const int r = first + lane;
         float x = (r + 1 <= e) ? sm[lds.alpha + r + 1] : 1.f;
 #pragma unroll
@@ -379,34 +380,25 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
           const float y = __shfl_down(x, d, kWave);
           if (lane + d < kWave) x *= y;
         }
-        if (r <= last) out[(r + 1) * stride] = (r <= e) ? x : 0.f;
+        if (r <= last) out[(r + 1) * TMAX] = (r <= e) ? x : 0.f;
       }
     } else {
-      if (outputs) {
-        for (int t = tid; t < R - r0 + 1; t += nthr) {
-          const int r = r0 - 1 + t;
-          float* gq = sm + lds.gq + (r + 1) * TMAX;
-          float* gk = sm + lds.gk + (r + 1) * TMAX;
-          for (int i = 0; i < TMAX; ++i) {
-            gq[i] = 0.f;
-            gk[i] = 0.f;
-          }
-          float prod = 1.f;
-          for (int rr = r + 1; rr < R; ++rr) {
-            const int i = rr - hc;
-            if (i >= 0) gk[i] = prod;
-            prod *= sm[lds.alpha + rr];
-            if (i >= 0) gq[i] = prod;
-          }
-          if (r >= hc) gq[r - hc] = 1.f;
+      for (int t = tid; t < R - r0 + 1; t += nthr) {
+        const int r = r0 - 1 + t;
+        float* gq = sm + lds.gq + (r + 1) * TMAX;
+        float* gk = sm + lds.gk + (r + 1) * TMAX;
+        for (int i = 0; i < TMAX; ++i) {
+          gq[i] = 0.f;
+          gk[i] = 0.f;
         }
-      }
-      if (fold) {
-        for (int t = tid; t <= hc; t += nthr) {
-          float prod = 1.f;
-          for (int rr = t; rr < hc; ++rr) prod *= sm[lds.alpha + rr];
-          sm[lds.gf + t] = prod;
+        float prod = 1.f;
+        for (int rr = r + 1; rr < R; ++rr) {
+          const int i = rr - hc;
+          if (i >= 0) gk[i] = prod;
+          prod *= sm[lds.alpha + rr];
+          if (i >= 0) gq[i] = prod;
         }
+        if (r >= hc) gq[r - hc] = 1.f;
       }
     }
   }
@@ -439,11 +431,20 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       }
     }
   }
-  __syncthreads();
+  };
 
   // ---- 3. fold: S <- Gamma_h S + sum_j gamma_j v_j k_j^T on MFMA ------------
-  if (fold) {
-    const float G = sm[lds.gf];
+  // The weights gf_t = prod of alpha over committed records [t, hc) (gf_0 =
+  // Gamma_h scales the checkpoint, gf_{j+1} weighs record j) are one
+  // suffix-product scan per wavefront: lane t holds gf_t, and gf_hc = 1.
+  auto fold_state = [&]() {
+    float gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const float y = __shfl_down(gf, d, kWave);
+      if (lane + d < kWave) gf *= y;
+    }
+    const float G = __shfl(gf, 0, kWave);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) S[nt] *= G;
     // MFMA 16x16x4: A[m][kk] = k_j[16 nt + m], B[kk][n] = gamma_j v_j[16 wave + n],
@@ -452,7 +453,8 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     for (int kc = 0; kc < nkc; ++kc) {
       const int j = 4 * kc + g;
       const bool vj = j < hc;
-      const float bval = vj ? sm[lds.gf + j + 1] * sm[lds.v + j * lds.dvs + prow] : 0.f;
+      const float wj = __shfl(gf, (j + 1) & (kWave - 1), kWave);  // gf_{j+1}; j + 1 = 64 only if hc = 64
+      const float bval = vj ? (j + 1 < kWave ? wj : 1.f) * sm[lds.v + j * lds.dvs + prow] : 0.f;
       const float* krow = sm + lds.k + (vj ? j : 0) * lds.dks + col;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -464,11 +466,10 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     if constexpr (NT >= 2) {
       if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, S, prec == REPLAYSSM_BF16_SHARED);
     }
-    if (outputs) matvec();
-    if (prefetch) load_ckpt_early<NT>(a, after_next, wave, lane, S);
-  }
+  };
 
   // ---- 4/5. outputs of the drafts ---------------------------------------------
+  auto write_outputs = [&]() {
   if (outputs) {
     const float* gq = sm + lds.gq;
     const float* gk = sm + lds.gk;
@@ -530,6 +531,21 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       }
     }
   }
+  };
+
+  // The fold (from the records already in LDS), the mat-vecs on the state the
+  // drafts start from, and the next item's checkpoint request, at one program
+  // point on every route: the compiler's waits are computed over every
+  // control-flow path, and a path without the request would make them drain.
+  if constexpr (NT >= 2) {
+    if (lp) widen_lp<NT>(S);  // (the shared-bf16 mode also folds from the bf16 values)
+  }
+  if (fold) fold_state();
+  if (outputs) matvec();
+  prefetch_next();
+  scans_and_dots();
+  __syncthreads();
+  write_outputs();
 
   // The item's last LDS reads are done once every wavefront is here.
   __syncthreads();
@@ -573,17 +589,8 @@ __device__ __forceinline__ void commit_pointers(const ReplayArgs& a, int tid, in
   }
 }
 
-// Checkpoint prefetch depth (1: the next item's; 2: also the one after, in a
-// second register buffer). Two buffers keep more bytes in flight per
-// workgroup but cost registers, hence occupancy.
-template <int KIND, int NT, int TMAX, bool FUSED>
-constexpr int prefetch_depth() {
-  return REPLAYSSM_PREFETCH_DEPTH;
-}
-
 template <int KIND, int NT, int TMAX, bool FUSED>
 __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
-  constexpr int DEPTH = prefetch_depth<KIND, NT, TMAX, FUSED>();
   extern __shared__ f32x4 smem_v4[];
   float* sm = reinterpret_cast<float*>(smem_v4);
   const int items = a.B * a.H;
@@ -600,6 +607,10 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
       phc = a.h[bb];
       pp = a.p[bb];
     }
+    // Wait for them here, once per batch. Left pending, they would be the
+    // newest loads on one path into the next item and the oldest on the other,
+    // and the wait at their first use would have to drain every load.
+    __asm__ volatile("" ::"v"(ph), "v"(phc), "v"(pp));
   };
   auto ptr_at = [&](int kl) {
     return SeqPtr{__builtin_amdgcn_readlane(ph, kl), __builtin_amdgcn_readlane(phc, kl),
@@ -608,45 +619,24 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   batch(blockIdx.x);  // (a workgroup without items still arrives at the end)
   SeqPtr ptr = ptr_at(0);
   Route rt = route_of(a, ptr);
-  if ((int)blockIdx.x >= items) rt.work = false;
-  // With two checkpoint buffers they are used alternately (the loop body is
-  // unrolled by two so that each has fixed registers): while one item
-  // computes, the next item's checkpoint and the one after it are in flight.
-  f32x4 SA[NT], SB[DEPTH == 2 ? NT : 1];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) SA[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (DEPTH == 2) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) SB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  const bool any = (int)blockIdx.x < items;
+  if (!any) rt.work = false;
+  f32x4 S[NT];
   RecRegs rr;
   {
     const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
-    load_records<KIND, NT, FUSED>(a, blockIdx.x, ptr, rt, threadIdx.x, map, rr);
+    load_records<KIND, NT, FUSED>(a, blockIdx.x, ptr, rt, any, threadIdx.x, map, rr);
   }
-  if (a.mode != kModeFlush && (int)blockIdx.x < items) {
-    load_ckpt_early<NT>(a, blockIdx.x, wave, lane, SA);
-    if constexpr (DEPTH == 2)
-      if ((int)blockIdx.x + G < items) load_ckpt_early<NT>(a, blockIdx.x + G, wave, lane, SB);
-  }
-  auto step = [&](int k, int item, f32x4 (&S)[NT]) {
+  prefetch_ckpt<NT>(a, blockIdx.x, rt.fold, any && rt.work, wave, lane, S);
+  for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) {
     const int next = item + G;
     const int kn = (k + 1) & 63;
     if (kn == 0 && next < items) batch(next);
     const SeqPtr nptr = ptr_at(kn);
     const Route nrt = route_of(a, nptr);
-    replay_item<KIND, NT, TMAX, FUSED>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt, DEPTH == 2 ? next + G : next);
+    replay_item<KIND, NT, TMAX, FUSED>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt);
     ptr = nptr;
     rt = nrt;
-  };
-  if constexpr (DEPTH == 2) {
-    for (int k = 0, item = blockIdx.x; item < items; k += 2, item += 2 * G) {
-      step(k, item, SA);
-      if (item + G >= items) break;
-      step(k + 1, item + G, SB);
-    }
-  } else {
-    for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) step(k, item, SA);
   }
 
   // Pointer commit. Each workgroup arrives once, after its last item (all its
