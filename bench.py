@@ -11,13 +11,12 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
 
   value      tokens/s of the whole step (B tokens per step), HIP-event timed over
              K steps after W warm-up steps, inputs already resident in HBM; a step
-             is one replayssm_decode_step launch (append + decode fused)
-  roofline   that kernel (the only one of the step): algorithmic bytes per launch
-             (checkpoint read, h+1 records, q, output, the new record's ring write,
-             checkpoint write on fold steps) / its average launch duration, both
-             measured live in a second pass with events around each launch, against
-             8 TB/s
-  unfused    the same step as replayssm_append + replayssm_decode
+             is replayssm_append of the token's record, then replayssm_decode
+  roofline   the decode kernel (the dominant one): algorithmic bytes per launch
+             (checkpoint read, h+1 records, q, output, checkpoint write on fold
+             steps) / its average launch duration, both measured live in a second
+             pass with events around each launch, against 8 TB/s
+  fused      the same step as one replayssm_decode_step launch
   eager      the conventional kernel that loads and stores the state every step
   workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint;
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
@@ -448,7 +447,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]
     sh = w.shape
-    main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed)
+    main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed, fused=False)
     fold_flops = 2 * sh.P * sh.N * w.L * sh.B * sh.H  # V diag(gamma) K^T over the L folded records
     tok_s = main_res["tokens"] / (main_res["ms"] * 1e-3)
     achieved = main_res["kernel_bytes"] / (main_res["kernel_ms_total"] * 1e6)
@@ -467,7 +466,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "kind": sh.kind, "B": sh.B, "H": sh.H, "P": sh.P, "N": sh.N, "L": w.L,
                    "T": 1, "precision": w.precision, "state_MiB_per_seq": sh.H * sh.P * sh.N * 4 / 2**20},
-        "roofline": {"bound": "hbm", "kernel": "replay_kernel (fused append + decode)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "replay_kernel (decode)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(), "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "avg_launch_us": main_res["kernel_avg_us"],
@@ -480,13 +479,14 @@ def main():
                          "frac": fold_flops / (main_res["fold_avg_us"] * 1e6) / MFMA_F32_PEAK_TFLOPS,
                          "flops_per_fold_step": fold_flops}},
         "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
-        "step": "replayssm_decode_step (append + decode in one launch)",
+        "step": "replayssm_append then replayssm_decode",
     }
     if not args.quick:
-        unf = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False)
-        line["unfused"] = {"tokens_per_s": unf["tokens"] / (unf["ms"] * 1e-3),
-                           "decode_kernel_gbs": unf["kernel_bytes"] / (unf["kernel_ms_total"] * 1e6),
-                           "step": "replayssm_append then replayssm_decode"}
+        fu = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=True)
+        line["fused"] = {"tokens_per_s": fu["tokens"] / (fu["ms"] * 1e-3),
+                         "kernel_gbs": fu["kernel_bytes"] / (fu["kernel_ms_total"] * 1e6),
+                         "kernel_avg_us": fu["kernel_avg_us"],
+                         "step": "replayssm_decode_step (append + decode in one launch)"}
     if not args.quick:
         eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
         line["eager"] = {"tokens_per_s": eg["tokens"] / (eg["ms"] * 1e-3), "gbs": eg["gbs"],

@@ -188,7 +188,8 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
                                            : s.rv + ring_slot(p.head, r, C) * dv + 4 * m.cv;
     rr.vb[j] = ld4(r < R ? src : a.ring_v);
   }
-  rr.qv = ld4(m.rk0 < T ? a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck : a.ring_k);
+  // q is read once per call: non-temporal, like the checkpoint stream
+  rr.qv = ld4_stream(m.rk0 < T ? a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck : a.ring_k);
   {
     const float* src = (fused && tid >= p.h) ? a.in_alpha + s.ia + (int64_t)(tid - p.h) * H
                                              : a.ring_alpha + s.bhC + ring_slot(p.head, tid, C);
@@ -232,7 +233,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     if (in && !GDN) st4(wv + slot * dv + 4 * m.cv, x);
   }
   for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
-    st4(sm + lds.q + i * DK + 4 * m.ck, ld4(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
+    st4(sm + lds.q + i * DK + 4 * m.ck, ld4_stream(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
   for (int r = tid + nthr; r < R; r += nthr) {
     const int slot = ring_slot(p.head, r, C);
     const bool in = fused && r >= p.h;
@@ -484,7 +485,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
           for (int r = r0 + g; r <= hc + i; r += 4)
             acc += gq[(r + 1) * TMAX + i] * cq[r * TMAX + i] * sv[r * lds.dvs];
           acc = sum_groups(acc);
-          if (g == 0) a.out[(((int64_t)b * T + i) * H + hd) * dv + prow] = acc;
+          if (g == 0) __builtin_nontemporal_store(acc, a.out + (((int64_t)b * T + i) * H + hd) * dv + prow);
         }
       }
     } else {
@@ -522,7 +523,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 #pragma unroll
           for (int d = 0; d <= i; ++d) o += gq[(hc + d + 1) * TMAX + i] * cq[(hc + d) * TMAX + i] * ud[d];
           if (g == 0) {
-            a.out[(((int64_t)b * T + i) * H + hd) * dv + prow] = o;
+            __builtin_nontemporal_store(o, a.out + (((int64_t)b * T + i) * H + hd) * dv + prow);
             int slot = head + hc + i;
             if (slot >= C) slot -= C;
             a.ring_v[(bh * C + slot) * dv + prow] = ud[i];
