@@ -1,6 +1,7 @@
 """Benchmark of the ReplaySSM decode path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick] [--sweep]
+                    [--window-sweep]
 
 A step of the headline workload is one standard decoding step of a Mamba-2 SSM
 layer at B=256, H=128, P=64, N=128 (4 MiB fp32 state per sequence), L=16:
@@ -22,6 +23,7 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
              each warm (one layer) and rotated (rounds cycle over layer instances
              holding >= 2 GiB of state, so the on-package cache cannot hold it)
+  window_sweep  with --window-sweep: L in {4..64} x T in {1, 4, 8} at the headline shape
   ceilings   practical HBM ceilings measured on the device: a read-only probe in
              the checkpoint stream's access pattern, and a device-to-device copy
   cpu_baseline  the CPU oracle (fp64 eager recurrence, OpenMP over heads) on a
@@ -85,6 +87,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
+    ap.add_argument("--window-sweep", action="store_true", help="also run the window-size sweep L x T")
     return ap.parse_args()
 
 
@@ -363,6 +366,49 @@ def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
     return {"ms": tm.ms, "steps": steps, "tokens": sh.B * T * steps, "bytes": b, "gbs": b / (tm.ms * 1e6)}
 
 
+def window_sweep(torch, rs, synth, seed):
+    """Window size L x drafts T at the headline layer shape (B=256, H=128, P=64, N=128, fp32):
+    standard decoding (append + decode) for T = 1, verify rounds with accepted prefix ~ U{0..T}
+    for T > 1. Per cell: throughput, the replay kernel's bandwidth, and algorithmic bytes per
+    (accepted) token, split into checkpoint bytes and the rest."""
+    import dataclasses
+
+    base = synth.WORKLOADS["mamba2_spec_b256"]
+    sh = base.shape
+    cells = {}
+    for L in (4, 8, 16, 32, 64):
+        for T in (1, 4, 8):
+            if T > L:
+                continue
+            key = f"L{L}_T{T}"
+            if L + T > 64 + 4:  # L = 64 with T = 8 exceeds the LDS budget (ENOTSUP)
+                cells[key] = "not supported (LDS budget)"
+                continue
+            w = dataclasses.replace(base, L=L, T=T, wid=base.wid + 1000 + 10 * L + T)
+            if T == 1:
+                r = run_standard_decode(torch, rs, synth, w, max(128, 2 * L), 16, seed, fused=False)
+                toks = r["tokens"]
+                cells[key] = {"tokens_per_s": toks / (r["ms"] * 1e-3),
+                              "kernel_gbs": r["kernel_bytes"] / (r["kernel_ms_total"] * 1e6),
+                              "kernel_avg_us": r["kernel_avg_us"],
+                              "bytes_per_token": (r["decode_bytes"] + r["append_bytes"]) / toks,
+                              "ckpt_bytes_per_token": 4 * sh.P * sh.N * (1 + 1.0 / L) * sh.H}
+            else:
+                r = run_spec(torch, rs, synth, w, 128, 16, seed, fused=False)
+                cells[key] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
+                              "drafts_per_s": r["drafts"] / (r["ms"] * 1e-3),
+                              "kernel_gbs": r["kernel_gbs"], "kernel_avg_us": r["kernel_avg_us"],
+                              "bytes_per_accepted_token": (r["verify_bytes"] + append_bytes(sh.kind, sh.P, sh.N, T)
+                                                           * sh.B * sh.H * r["rounds"]) / max(r["accepted_tokens"], 1)}
+    best = {}
+    for T in (1, 4, 8):
+        vals = {k: v.get("tokens_per_s", v.get("accepted_tokens_per_s")) for k, v in cells.items()
+                if isinstance(v, dict) and k.endswith(f"_T{T}")}
+        if vals:
+            best[f"T{T}"] = max(vals, key=vals.get)
+    return {"cells": cells, "best": best, "shape": "Mamba-2 B=256 H=128 P=64 N=128 fp32"}
+
+
 def ceilings(torch, rs):
     """Practical HBM ceilings of the device: the read probe (the decode kernel's checkpoint access
     pattern, read-only) over 4 GiB, and a 2 GiB device-to-device copy (2 bytes moved per byte)."""
@@ -528,8 +574,10 @@ def main():
                         "layers": r["layers"], "layer_footprint_MiB": round(r["layer_footprint_MiB"], 1)}
             r4["batch_sweep_fp32_hp_bf16_lp"] = sweep
         wl[w4.name] = r4
-        line["ceilings"] = ceilings(torch, rs)
         line["workloads"] = wl
+        line["ceilings"] = ceilings(torch, rs)
+    if args.window_sweep:
+        line["window_sweep"] = window_sweep(torch, rs, synth, args.seed)
     if not (args.quick or args.no_cpu_baseline):
         line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds)
         if not args.quick:

@@ -65,9 +65,9 @@ int check_config(const replayssm_config* c) {
                 "bf16 checkpoints are built for Mamba-2 only: a GDN correction computed from "
                 "the bf16 copy would carry its rounding into the recurrence");
   const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max));
-  if (lds.total * 4 > 64 * 1024)
-    return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> 64 KiB)",
-                lds.total * 4);
+  if (lds.total * 4 > rs::kMaxLdsBytes)
+    return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
+                rs::kMaxLdsBytes);
   return REPLAYSSM_OK;
 }
 

@@ -94,15 +94,21 @@ struct EagerArgs {
 
 // Dynamic LDS carve-up of the replay kernel, in floats. Every block starts on a
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
-// wavefront reading one column of four consecutive rows hit distinct banks.
+// wavefront reading one column of four consecutive rows hit distinct banks;
+// windows too long for that within kMaxLdsBytes use unpadded rows instead.
+constexpr int kMaxLdsBytes = 64 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
   int k, v, alpha, beta, q, gq, gk, cq, ck, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
   __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
-    dks = row_stride(dk);
-    dvs = row_stride(dv);
+    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv));
+    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv);
+  }
+  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride) {
+    dks = kstride;
+    dvs = vstride;
     k = 0;
     v = k + C * dks;
     alpha = v + C * dvs;
