@@ -123,11 +123,17 @@ def replay_launch_bytes(kind, precision, P, N, h, T, fold, fused=False):
         b += T * 4 * P  # u written back into the ring
     if fold:
         b += ckpt_write_bytes(precision, P, N)
+    if kind == "gdn" and precision == "fp32_hp_bf16_lp":
+        if fold:
+            b += h * (4 * P + 4)  # the folded records' raw v and beta, to recompute their u
+        if fused:
+            b += T * 4 * P  # the drafts' raw v kept for the fold
     return b
 
 
-def append_bytes(kind, P, N, T):
-    return 2 * T * record_bytes(kind, P, N)  # read the inputs, write the ring
+def append_bytes(kind, P, N, T, precision="fp32"):
+    extra = T * 4 * P if (kind == "gdn" and precision == "fp32_hp_bf16_lp") else 0  # raw v copy
+    return 2 * T * record_bytes(kind, P, N) + extra  # read the inputs, write the ring
 
 
 def eager_bytes(kind, P, N, T, snapshots):
@@ -195,7 +201,7 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
         nfold += fold
         h = 1 if fold else h + 1
     res = {"ms": tm.ms, "steps": steps, "tokens": sh.B * steps, "decode_bytes": kbytes * sh.B * sh.H,
-           "append_bytes": 0 if fused else append_bytes(sh.kind, sh.P, sh.N, 1) * sh.B * sh.H * steps,
+           "append_bytes": 0 if fused else append_bytes(sh.kind, sh.P, sh.N, 1, w.precision) * sh.B * sh.H * steps,
            "folds": nfold, "fused": fused}
     if kernel_pass:
         # second pass: events around every decode launch (same stream as the kernels)
@@ -552,11 +558,15 @@ def main():
         r3 = run_standard_decode(torch, rs, synth, w3, 256, 16, args.seed)
         e3 = run_eager(torch, rs, synth, w3, 256, 16, args.seed)
         r3s = run_spec(torch, rs, synth, w3, 64, 8, args.seed)
+        r3p = run_spec(torch, rs, synth, w3, 64, 8, args.seed, precision="fp32_hp_bf16_lp")
         wl[w3.name] = {"tokens_per_s": r3["tokens"] / (r3["ms"] * 1e-3),
                        "decode_kernel_gbs": r3["kernel_bytes"] / (r3["kernel_ms_total"] * 1e6),
                        "eager_tokens_per_s": e3["tokens"] / (e3["ms"] * 1e-3), "eager_gbs": e3["gbs"],
                        "verify_T4_accepted_tokens_per_s": r3s["accepted_tokens"] / (r3s["ms"] * 1e-3),
-                       "verify_T4_kernel_gbs": r3s["kernel_gbs"]}
+                       "verify_T4_kernel_gbs": r3s["kernel_gbs"], "verify_T4_avg_us": r3s["kernel_avg_us"],
+                       "two_precision_verify_T4_accepted_tokens_per_s": r3p["accepted_tokens"] / (r3p["ms"] * 1e-3),
+                       "two_precision_verify_T4_kernel_gbs": r3p["kernel_gbs"],
+                       "two_precision_verify_T4_avg_us": r3p["kernel_avg_us"]}
         w4 = synth.WORKLOADS["mamba2_2prec_b256"]
         r4 = {}
         for prec in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):

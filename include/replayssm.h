@@ -67,7 +67,10 @@ enum replayssm_kind {
 enum replayssm_precision {
   REPLAYSSM_FP32 = 0,          /* one fp32 checkpoint (HP), read every step          */
   REPLAYSSM_FP32_HP_BF16_LP = 1, /* non-fold steps read a bf16 copy (LP); folds read
-                                    HP and write HP and LP (Mamba-2 only)           */
+                                    HP and write HP and LP. GDN: a fold recomputes
+                                    every folded record's u from HP and the raw v
+                                    (ring_vraw), so the bf16 rounding of the copy
+                                    never enters the checkpoint                     */
   REPLAYSSM_BF16_SHARED = 2    /* one bf16 checkpoint for reads and folds (Mamba-2
                                   only); the comparison case for the two-precision
                                   mode                                              */
@@ -95,7 +98,10 @@ typedef struct replayssm_config {
  *  ring_v      float  [B][H][C][dv]  Mamba-2: v. GDN: v as appended, replaced by
  *                                    the correction u_t = beta_t (v_t - alpha_t
  *                                    S_{t-1} k_t) by the decode/verify call that
- *                                    consumes the record
+ *                                    consumes the record (computed from the
+ *                                    checkpoint copy that call reads)
+ *  ring_vraw   float  [B][H][C][dv]  GDN in FP32_HP_BF16_LP mode only, else NULL:
+ *                                    v as appended, kept for the fold
  *  head, h, p  int32  [B]            ring slot of the oldest unfolded committed
  *                                    record; committed unfolded records; pending
  *                                    drafts
@@ -118,6 +124,7 @@ typedef struct replayssm_state {
   int64_t* folded;
   int32_t* arrive;
   int32_t* err;
+  float* ring_vraw;
 } replayssm_state;
 
 typedef struct replayssm_sizes {
@@ -132,6 +139,7 @@ typedef struct replayssm_sizes {
   int64_t ptr_bytes;       /* each of head, h, p, arrive                       */
   int64_t folded_bytes;
   int64_t err_bytes;
+  int64_t ring_vraw_bytes; /* GDN with FP32_HP_BF16_LP only, else 0            */
 } replayssm_sizes;
 
 /* ---- helpers ------------------------------------------------------------ */

@@ -42,14 +42,14 @@ class Config(ctypes.Structure):
 class State(ctypes.Structure):
     _fields_ = [("hp", _vp), ("lp", _vp), ("ring_alpha", _vp), ("ring_beta", _vp), ("ring_k", _vp),
                 ("ring_v", _vp), ("head", _vp), ("h", _vp), ("p", _vp), ("folded", _vp),
-                ("arrive", _vp), ("err", _vp)]
+                ("arrive", _vp), ("err", _vp), ("ring_vraw", _vp)]
 
 
 class Sizes(ctypes.Structure):
     _fields_ = [("C", _i32), ("alignment", _i32), ("hp_bytes", _i64), ("lp_bytes", _i64),
                 ("ring_alpha_bytes", _i64), ("ring_beta_bytes", _i64), ("ring_k_bytes", _i64),
                 ("ring_v_bytes", _i64), ("ptr_bytes", _i64), ("folded_bytes", _i64),
-                ("err_bytes", _i64)]
+                ("err_bytes", _i64), ("ring_vraw_bytes", _i64)]
 
 
 class ReplaySSMError(RuntimeError):
@@ -250,9 +250,10 @@ class LayerState:
         self.folded = torch.zeros(B, dtype=torch.int64, device=device)
         self.arrive = torch.zeros(B, dtype=i32, device=device)
         self.err = torch.zeros(4, dtype=i32, device=device)
+        self.ring_vraw = torch.zeros((B, H, C, dv), dtype=f32, device=device) if sz.ring_vraw_bytes else None
         self.struct = State(*[None if t is None else t.data_ptr() for t in (
             self.hp, self.lp, self.ring_alpha, self.ring_beta, self.ring_k, self.ring_v, self.head,
-            self.h, self.p, self.folded, self.arrive, self.err)])
+            self.h, self.p, self.folded, self.arrive, self.err, self.ring_vraw)])
         init(cfg, self.struct, stream)
 
     def import_state(self, S_logical: torch.Tensor, stream=None):
@@ -272,7 +273,7 @@ class LayerState:
     def tensors(self):
         """Every device tensor the layer's state holds."""
         return [t for t in (self.hp, self.lp, self.ring_alpha, self.ring_beta, self.ring_k, self.ring_v, self.head,
-                            self.h, self.p, self.folded, self.arrive, self.err) if t is not None]
+                            self.h, self.p, self.folded, self.arrive, self.err, self.ring_vraw) if t is not None]
 
     def pointers(self):
         return {"head": self.head.tolist(), "h": self.h.tolist(), "p": self.p.tolist(),

@@ -42,6 +42,11 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 
 int tmax_bucket(int T) { return T <= 1 ? 1 : (T <= 4 ? 4 : 8); }
 
+// GDN with the two-precision checkpoint recomputes the folded records' corrections.
+bool exact_u(const replayssm_config* c) {
+  return c->kind == REPLAYSSM_GDN && c->precision == REPLAYSSM_FP32_HP_BF16_LP;
+}
+
 int check_config(const replayssm_config* c) {
   if (c == nullptr) return fail(REPLAYSSM_EINVAL, "cfg is NULL");
   if (c->kind != REPLAYSSM_MAMBA2 && c->kind != REPLAYSSM_GDN)
@@ -60,11 +65,11 @@ int check_config(const replayssm_config* c) {
     return fail(REPLAYSSM_EINVAL, "T_max=%d outside 1..min(8, L)", c->T_max);
   if (c->precision != REPLAYSSM_FP32 && c->dk % 32 != 0)
     return fail(REPLAYSSM_ENOTSUP, "a bf16 checkpoint needs dk %% 32 == 0 (dk=%d)", c->dk);
-  if (c->precision != REPLAYSSM_FP32 && c->kind == REPLAYSSM_GDN)
+  if (c->precision == REPLAYSSM_BF16_SHARED && c->kind == REPLAYSSM_GDN)
     return fail(REPLAYSSM_ENOTSUP,
-                "bf16 checkpoints are built for Mamba-2 only: a GDN correction computed from "
-                "the bf16 copy would carry its rounding into the recurrence");
-  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max));
+                "the shared bf16 checkpoint is built for Mamba-2 only (GDN takes FP32 or "
+                "FP32_HP_BF16_LP)");
+  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max), exact_u(c));
   if (lds.total * 4 > rs::kMaxLdsBytes)
     return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
                 rs::kMaxLdsBytes);
@@ -79,6 +84,7 @@ int check_state(const replayssm_config* c, const replayssm_state* s) {
   NEED(s->ring_k);
   NEED(s->ring_v);
   if (c->kind == REPLAYSSM_GDN) NEED(s->ring_beta);
+  if (exact_u(c)) NEED(s->ring_vraw);
   NEED(s->head);
   NEED(s->h);
   NEED(s->p);
@@ -97,6 +103,7 @@ rs::ReplayArgs replay_args(const replayssm_config* c, const replayssm_state* s, 
   a.ring_beta = s->ring_beta;
   a.ring_k = s->ring_k;
   a.ring_v = s->ring_v;
+  a.ring_vraw = exact_u(c) ? s->ring_vraw : nullptr;
   a.head = s->head;
   a.h = s->h;
   a.p = s->p;
@@ -156,6 +163,7 @@ int replayssm_get_sizes(const replayssm_config* cfg, replayssm_sizes* out) {
   out->ptr_bytes = (int64_t)cfg->B * 4;
   out->folded_bytes = (int64_t)cfg->B * 8;
   out->err_bytes = 4;
+  out->ring_vraw_bytes = exact_u(cfg) ? BH * C * cfg->dv * 4 : 0;
   return REPLAYSSM_OK;
 }
 
@@ -222,6 +230,7 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
   a.ring_beta = st->ring_beta;
   a.ring_k = st->ring_k;
   a.ring_v = st->ring_v;
+  a.ring_vraw = exact_u(cfg) ? st->ring_vraw : nullptr;
   a.head = st->head;
   a.h = st->h;
   a.p = st->p;

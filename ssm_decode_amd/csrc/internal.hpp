@@ -35,6 +35,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Mode : int { kModeDecode = 0, kModeVerify = 1, kModeFlush = 2 };
 
+// Kernel kinds: the two public kinds, plus GDN with the two-precision checkpoint,
+// whose fold recomputes the folded records' corrections (its own instantiation,
+// so that the FP32 GDN kernels do not carry that code's registers).
+constexpr int kKindGdnExact = 2;
+__host__ __device__ constexpr bool kind_gdn(int kind) { return kind != REPLAYSSM_MAMBA2; }
+
 struct ReplayArgs {
   float* hp;
   uint16_t* lp;
@@ -48,6 +54,7 @@ struct ReplayArgs {
   int64_t* folded;
   int32_t* arrive;
   int32_t* err;
+  float* ring_vraw;  // GDN two-precision: raw v of every record, for the fold
   const float* q;  // [B][T][H][dk]
   float* out;      // [B][T][H][dv]
   // fused append: the T new records come from these inputs (and are written to
@@ -67,6 +74,7 @@ struct AppendArgs {
   float* ring_beta;
   float* ring_k;
   float* ring_v;
+  float* ring_vraw;  // or NULL
   int32_t* head;
   int32_t* h;
   int32_t* p;
@@ -96,17 +104,20 @@ struct EagerArgs {
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
 // wavefront reading one column of four consecutive rows hit distinct banks;
 // windows too long for that within kMaxLdsBytes use unpadded rows instead.
+// With exact_u (GDN, two-precision) three more blocks serve the fold's
+// recomputation of the corrections: beta of the committed records, S_ck k_j for
+// every committed record, and the records' Gram matrix k_i . k_j.
 constexpr int kMaxLdsBytes = 64 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, br, y, gram, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
-  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
-    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv));
-    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv);
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, bool exact_u = false) {
+    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), exact_u);
+    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, exact_u);
   }
-  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride) {
+  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, bool exact_u) {
     dks = kstride;
     dvs = vstride;
     k = 0;
@@ -118,7 +129,10 @@ struct ReplayLds {
     gk = gq + pad4((C + 1) * tmax);
     cq = gk + pad4((C + 1) * tmax);
     ck = cq + pad4(C * tmax);
-    total = ck + pad4(C * tmax);
+    br = ck + pad4(C * tmax);
+    y = br + (exact_u ? pad4(C) : 0);
+    gram = y + (exact_u ? C * dv : 0);
+    total = gram + (exact_u ? pad4(C * C) : 0);
   }
 };
 

@@ -141,6 +141,7 @@ __device__ __forceinline__ int ring_slot(int head, int r, int C) {
 struct RowSrc {
   const float* rk;   // ring k rows of the head
   const float* rv;   // ring v rows
+  const float* rvraw;  // raw v rows (GDN, two-precision), else the same as rv
   const float* ik;   // input k of draft 0 (fused), stride H * dk per draft
   const float* iv;   // input v of draft 0 (fused), stride H * dv per draft
   int64_t ia;        // index of draft 0 in the alpha / beta inputs, stride H per draft
@@ -156,6 +157,7 @@ __device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) 
   RowSrc s;
   s.rk = a.ring_k + bh * (int64_t)C * DK;
   s.rv = a.ring_v + bh * (int64_t)C * dv;
+  s.rvraw = a.ring_vraw ? a.ring_vraw + bh * (int64_t)C * dv : s.rv;
   s.ia = (int64_t)b * T * H + hd;
   s.ik = a.in_k + s.ia * DK;
   s.iv = a.in_v + s.ia * dv;
@@ -181,11 +183,14 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
                                            : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck;
     rr.kb[j] = ld4(r < R ? src : a.ring_k);
   }
+  // a fold of the exact-correction kind stages the committed records' raw v (it
+  // recomputes their corrections); every other item stages the stored rows
+  const bool raw = KIND == kKindGdnExact && rt.fold;
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
     const int r = m.rv0 + j * 16;
     const float* src = (fused && r >= p.h) ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
-                                           : s.rv + ring_slot(p.head, r, C) * dv + 4 * m.cv;
+                                           : (raw && r < p.h ? s.rvraw : s.rv) + ring_slot(p.head, r, C) * dv + 4 * m.cv;
     rr.vb[j] = ld4(r < R ? src : a.ring_v);
   }
   // q is read once per call: non-temporal, like the checkpoint stream
@@ -195,10 +200,10 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
                                              : a.ring_alpha + s.bhC + ring_slot(p.head, tid, C);
     rr.al = *(tid < R ? src : a.ring_alpha);
   }
-  if (KIND == REPLAYSSM_GDN) {
-    const float* src = fused ? a.in_beta + s.ia + (int64_t)(tid - p.h) * H
-                             : a.ring_beta + s.bhC + ring_slot(p.head, tid, C);
-    rr.be = *((tid < R && tid >= p.h) ? src : a.ring_beta);
+  if constexpr (kind_gdn(KIND)) {
+    const float* src = (fused && tid >= p.h) ? a.in_beta + s.ia + (int64_t)(tid - p.h) * H
+                                             : a.ring_beta + s.bhC + ring_slot(p.head, tid, C);
+    rr.be = *((tid < R && (tid >= p.h || raw)) ? src : a.ring_beta);
   }
 }
 
@@ -211,7 +216,8 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
                                               const SeqPtr& p, const Route& rt, int tid, int nthr,
                                               const StageMap& m, const RecRegs& rr) {
   constexpr int DK = NT * 16;
-  constexpr bool GDN = (KIND == REPLAYSSM_GDN);
+  constexpr bool GDN = kind_gdn(KIND);
+  const bool raw = KIND == kKindGdnExact && rt.fold;
   const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
   const int b = item / H, hd = item - b * H;
   const RowSrc s = row_src<NT>(a, item, T);
@@ -228,9 +234,11 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   for (int r = m.rv0 + kRecV * 16; r < R; r += 16) {
     const int slot = ring_slot(p.head, r, C);
     const bool in = fused && r >= p.h;
-    const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv : s.rv + slot * dv + 4 * m.cv);
+    const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
+                           : (raw && r < p.h ? s.rvraw : s.rv) + slot * dv + 4 * m.cv);
     st4(sm + lds.v + r * lds.dvs + 4 * m.cv, x);
     if (in && !GDN) st4(wv + slot * dv + 4 * m.cv, x);
+    if (in && GDN && a.ring_vraw) st4(a.ring_vraw + (s.rv - a.ring_v) + slot * dv + 4 * m.cv, x);
   }
   for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
     st4(sm + lds.q + i * DK + 4 * m.ck, ld4_stream(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
@@ -240,9 +248,10 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
     sm[lds.alpha + r] = al;
     if (in) a.ring_alpha[s.bhC + slot] = al;
-    if (GDN && r >= p.h) {
+    if (GDN && (r >= p.h || raw)) {
       const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
-      sm[lds.beta + (r - p.h)] = be;
+      if (r >= p.h) sm[lds.beta + (r - p.h)] = be;
+      if (raw) sm[lds.br + r] = be;
       if (in) a.ring_beta[s.bhC + slot] = be;
     }
   }
@@ -260,6 +269,8 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     if (r < R) {
       st4(sm + lds.v + r * lds.dvs + 4 * m.cv, rr.vb[j]);
       if (!GDN && fused && r >= p.h) st4(wv + ring_slot(p.head, r, C) * dv + 4 * m.cv, rr.vb[j]);
+      if (GDN && fused && r >= p.h && a.ring_vraw)
+        st4(a.ring_vraw + (s.rv - a.ring_v) + ring_slot(p.head, r, C) * dv + 4 * m.cv, rr.vb[j]);
     }
   }
   if (m.rk0 < T) st4(sm + lds.q + m.rk0 * DK + 4 * m.ck, rr.qv);
@@ -268,9 +279,10 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   if (tid < R) {
     sm[lds.alpha + tid] = rr.al;
     if (fused && tid >= p.h) a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)] = rr.al;
-    if (GDN && tid >= p.h) {
-      sm[lds.beta + (tid - p.h)] = rr.be;
-      if (fused) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
+    if (GDN && (tid >= p.h || raw)) {
+      if (tid >= p.h) sm[lds.beta + (tid - p.h)] = rr.be;
+      if (raw) sm[lds.br + tid] = rr.be;
+      if (fused && tid >= p.h) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
     }
   }
 }
@@ -286,7 +298,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   constexpr int DK = NT * 16;
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
   constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
-  constexpr bool GDN = (KIND == REPLAYSSM_GDN);
+  constexpr bool GDN = kind_gdn(KIND);
 
   // The thread index is laundered per item: without it the compiler hoists
   // every thread-derived address out of the item loop and keeps them all live
@@ -304,7 +316,8 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int hd = item - b * H;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
-  const ReplayLds lds(C, DK, dv, TMAX);
+  constexpr bool exact_u = KIND == kKindGdnExact;
+  const ReplayLds lds(C, DK, dv, TMAX, exact_u);
   const StageMap map(tid, nthr, LPR, dv);
 
   const int mode = a.mode;
@@ -438,7 +451,68 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // The weights gf_t = prod of alpha over committed records [t, hc) (gf_0 =
   // Gamma_h scales the checkpoint, gf_{j+1} weighs record j) are one
   // suffix-product scan per wavefront: lane t holds gf_t, and gf_hc = 1.
+  // GDN with the two-precision checkpoint: the u stored with each committed
+  // record was computed from the bf16 copy. The fold recomputes them from the
+  // fp32 checkpoint in S and the records' raw v, so that the copy's rounding never
+  // reaches the checkpoint ("How it works": Gated DeltaNet and Two precisions).
+  // With D_j = prod_{m<j} alpha_m and g_ij = prod_{m=i+1..j-1} alpha_m, the state
+  // before record j applied to k_j is w_j = D_j (S_ck k_j) + sum_{i<j} g_ij
+  // (k_i . k_j) u_i, and u_j = beta_j (v_j - alpha_j w_j).
+  // The committed records' raw v and beta were staged in place of their stored
+  // corrections (LDS v rows, and lds.br) with the other rows.
+  auto exact_corrections = [&]() {
+    // Gram matrix of the committed keys, i < j
+    for (int id = tid; id < hc * hc; id += nthr) {
+      const int i = id / hc, j = id - i * hc;
+      if (i < j) {
+        float c = 0.f;
+        for (int n = 0; n < DK; n += 4)
+          c += dot4(ld4(sm + lds.k + i * lds.dks + n), ld4(sm + lds.k + j * lds.dks + n));
+        sm[lds.gram + i * C + j] = c;
+      }
+    }
+    // S_ck k_j on MFMA (16 records per block): lane l supplies A[l & 15][l >> 4] =
+    // k_{16 jb + (l & 15)}[16 nt + 4 (l >> 4) + c] and B[l >> 4][l & 15] = its own
+    // S[nt][c]; the block result gives lane l its row's values for records
+    // 16 jb + 4 (l >> 4) + i, i = 0..3.
+    for (int jb = 0; 16 * jb < hc; ++jb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int ja = 16 * jb + col;
+      const float* krow = sm + lds.k + (ja < hc ? ja : 0) * lds.dks + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ja < hc ? krow[16 * nt + c] : 0.f, S[nt][c], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * jb + 4 * g + i;
+        if (j < hc) sm[lds.y + j * dv + prow] = acc[i];
+      }
+    }
+    __syncthreads();
+    // the recurrence over the records, one thread per state row; u_j replaces
+    // v_j in the LDS row the fold reads
+    for (int p = tid; p < dv; p += nthr) {
+      float D = 1.f;
+      for (int j = 0; j < hc; ++j) {
+        float w = D * sm[lds.y + j * dv + p];
+        float gij = 1.f;
+        for (int i = j - 1; i >= 0; --i) {
+          w += gij * sm[lds.gram + i * C + j] * sm[lds.v + i * lds.dvs + p];
+          gij *= sm[lds.alpha + i];
+        }
+        const float al = sm[lds.alpha + j];
+        sm[lds.v + j * lds.dvs + p] = sm[lds.br + j] * (sm[lds.v + j * lds.dvs + p] - al * w);
+        D *= al;
+      }
+    }
+    __syncthreads();
+  };
+
   auto fold_state = [&]() {
+    if constexpr (exact_u) exact_corrections();
     float gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -653,7 +727,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
 
 template <int KIND, int NT, int TMAX, bool FUSED>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX);
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND == kKindGdnExact);
   const int block = a.dv / 16 * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
@@ -693,6 +767,8 @@ static hipError_t launch_kind(int dk, int tmax, const ReplayArgs& a, hipStream_t
 
 hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
+  if (kind == REPLAYSSM_GDN && a.precision == REPLAYSSM_FP32_HP_BF16_LP)
+    return launch_kind<kKindGdnExact>(dk, tmax, a, s);
   return kind == REPLAYSSM_GDN ? launch_kind<REPLAYSSM_GDN>(dk, tmax, a, s)
                                : launch_kind<REPLAYSSM_MAMBA2>(dk, tmax, a, s);
 }

@@ -75,7 +75,10 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
         const int c4 = uv % dv4, th = uv / dv4;
         const int hd = th % H, i = th / H;
         const int slot = (first + i) % C;
-        st4(a.ring_v + (((int64_t)b * H + hd) * C + slot) * dv + 4 * c4, ld4(vsrc + 4 * (int64_t)uv));
+        const int64_t dst = (((int64_t)b * H + hd) * C + slot) * dv + 4 * c4;
+        const f32x4 x = ld4(vsrc + 4 * (int64_t)uv);
+        st4(a.ring_v + dst, x);
+        if (KIND == REPLAYSSM_GDN && a.ring_vraw) st4(a.ring_vraw + dst, x);
       }
     }
     if (blockIdx.x == 0) {

@@ -61,7 +61,10 @@ def test_sizes_of_the_b256_mamba2_layer(rs):
     s3 = rs.get_sizes(rs.make_config("mamba2", "bf16_shared", 2, 2, 64, 128, 16, 4))
     assert s3.hp_bytes == 0 and s3.lp_bytes > 0
     s4 = rs.get_sizes(rs.make_config("gdn", "fp32", 256, 32, 128, 128, 16, 4))
-    assert s4.ring_beta_bytes == 256 * 32 * 20 * 4
+    assert s4.ring_beta_bytes == 256 * 32 * 20 * 4 and s4.ring_vraw_bytes == 0
+    s5 = rs.get_sizes(rs.make_config("gdn", "fp32_hp_bf16_lp", 256, 32, 128, 128, 16, 4))
+    assert s5.ring_vraw_bytes == s5.ring_v_bytes == 256 * 32 * 20 * 128 * 4 and s5.lp_bytes == s5.hp_bytes // 2
+    assert s2.ring_vraw_bytes == 0
 
 
 @pytest.mark.parametrize("L,T", [(4, 1), (4, 4), (8, 8), (16, 8), (32, 8), (64, 1), (64, 4)])
@@ -77,6 +80,7 @@ def test_window_sweep_configs_fit(rs, L, T):
     (dict(dv=24), -1), (dict(dv=272), -1), (dict(dk=48), -1), (dict(dk=256), -1), (dict(L=0), -1),
     (dict(L=65), -1), (dict(T_max=0), -1), (dict(T_max=9, L=16), -1), (dict(T_max=5, L=4), -1),
     (dict(precision="fp32_hp_bf16_lp", dk=16, dv=16), -2), (dict(kind="gdn", precision="bf16_shared"), -2),
+    (dict(kind="gdn", precision="fp32_hp_bf16_lp", L=64, T_max=4, dv=128), -2),
     (dict(L=64, T_max=8, dv=256, dk=128), -2), (dict(L=64, T_max=8), -2),
 ])
 def test_config_validation(rs, kw, code):
@@ -96,7 +100,7 @@ def test_calls_reject_bad_arguments_before_enqueueing(rs):
     assert L.replayssm_init(ctypes.byref(cfg), None, None) == rs.EINVAL
     assert L.replayssm_decode(None, ctypes.byref(st), None, None, None) == rs.EINVAL
     fake = 1 << 20  # aligned, never dereferenced: validation fails first
-    st_ok = rs.State(*([fake] * 12))
+    st_ok = rs.State(*([fake] * 13))
     st_ok.lp = None
     st_ok.ring_beta = None
     assert L.replayssm_append(ctypes.byref(cfg), ctypes.byref(st_ok), 0, fake, fake, fake, None, None) == rs.EINVAL
