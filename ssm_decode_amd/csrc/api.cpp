@@ -31,6 +31,10 @@ int hip_result(hipError_t e, const char* what) {
   return fail(REPLAYSSM_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+hipError_t replay(const replayssm_config* cfg, int tmax, const rs::ReplayArgs& a, hipStream_t s) {
+  return rs::launch_replay(cfg->kind, cfg->dk, tmax, a, s);
+}
+
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Pointer must be non-NULL and 16-byte aligned.
@@ -42,7 +46,8 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 
 int tmax_bucket(int T) { return T <= 1 ? 1 : (T <= 4 ? 4 : 8); }
 
-// GDN with the two-precision checkpoint recomputes the folded records' corrections.
+// GDN with the two-precision checkpoint keeps the raw v of every record: its folds
+// recompute the folded records' corrections from the fp32 checkpoint.
 bool exact_u(const replayssm_config* c) {
   return c->kind == REPLAYSSM_GDN && c->precision == REPLAYSSM_FP32_HP_BF16_LP;
 }
@@ -69,7 +74,7 @@ int check_config(const replayssm_config* c) {
     return fail(REPLAYSSM_ENOTSUP,
                 "the shared bf16 checkpoint is built for Mamba-2 only (GDN takes FP32 or "
                 "FP32_HP_BF16_LP)");
-  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max), exact_u(c));
+  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max));
   if (lds.total * 4 > rs::kMaxLdsBytes)
     return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
                 rs::kMaxLdsBytes);
@@ -258,7 +263,7 @@ int replayssm_decode(const replayssm_config* cfg, const replayssm_state* st, con
   NEED(q);
   NEED(out);
   const rs::ReplayArgs a = replay_args(cfg, st, 1, rs::kModeDecode, q, out);
-  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, 1, a, as_stream(stream)), "decode");
+  return hip_result(replay(cfg, 1, a, as_stream(stream)), "decode");
 }
 
 int replayssm_verify(const replayssm_config* cfg, const replayssm_state* st, int T, const float* q,
@@ -269,7 +274,7 @@ int replayssm_verify(const replayssm_config* cfg, const replayssm_state* st, int
   NEED(q);
   NEED(out);
   const rs::ReplayArgs a = replay_args(cfg, st, T, rs::kModeVerify, q, out);
-  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, tmax_bucket(T), a, as_stream(stream)),
+  return hip_result(replay(cfg, tmax_bucket(T), a, as_stream(stream)),
                     "verify");
 }
 
@@ -291,7 +296,7 @@ static int fused_call(const replayssm_config* cfg, const replayssm_state* st, in
   a.in_k = k;
   a.in_v = v;
   a.fused = 1;
-  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, tmax_bucket(T), a, as_stream(stream)), what);
+  return hip_result(replay(cfg, tmax_bucket(T), a, as_stream(stream)), what);
 }
 
 int replayssm_decode_step(const replayssm_config* cfg, const replayssm_state* st, const float* alpha,
@@ -320,7 +325,7 @@ int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void
   if (int r = check_config(cfg)) return r;
   if (int r = check_state(cfg, st)) return r;
   const rs::ReplayArgs a = replay_args(cfg, st, 0, rs::kModeFlush, nullptr, nullptr);
-  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, 1, a, as_stream(stream)), "flush");
+  return hip_result(replay(cfg, 1, a, as_stream(stream)), "flush");
 }
 
 int replayssm_eager_step(const replayssm_config* cfg, float* S, const float* alpha, const float* k,

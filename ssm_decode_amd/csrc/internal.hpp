@@ -36,8 +36,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 enum Mode : int { kModeDecode = 0, kModeVerify = 1, kModeFlush = 2 };
 
 // Kernel kinds: the two public kinds, plus GDN with the two-precision checkpoint,
-// whose fold recomputes the folded records' corrections (its own instantiation,
-// so that the FP32 GDN kernels do not carry that code's registers).
+// whose folds recompute the folded records' corrections (its own instantiation,
+// so that the other GDN kernels do not carry that code's registers).
 constexpr int kKindGdnExact = 2;
 __host__ __device__ constexpr bool kind_gdn(int kind) { return kind != REPLAYSSM_MAMBA2; }
 
@@ -104,35 +104,29 @@ struct EagerArgs {
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
 // wavefront reading one column of four consecutive rows hit distinct banks;
 // windows too long for that within kMaxLdsBytes use unpadded rows instead.
-// With exact_u (GDN, two-precision) three more blocks serve the fold's
-// recomputation of the corrections: beta of the committed records, S_ck k_j for
-// every committed record, and the records' Gram matrix k_i . k_j.
 constexpr int kMaxLdsBytes = 64 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, br, y, gram, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
-  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, bool exact_u = false) {
-    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), exact_u);
-    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, exact_u);
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
+    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv));
+    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv);
   }
-  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, bool exact_u) {
+  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride) {
     dks = kstride;
     dvs = vstride;
     k = 0;
     v = k + C * dks;
     alpha = v + C * dvs;
     beta = alpha + pad4(C);
-    q = beta + pad4(tmax);
+    q = beta + pad4(C);
     gq = q + tmax * dk;
     gk = gq + pad4((C + 1) * tmax);
     cq = gk + pad4((C + 1) * tmax);
     ck = cq + pad4(C * tmax);
-    br = ck + pad4(C * tmax);
-    y = br + (exact_u ? pad4(C) : 0);
-    gram = y + (exact_u ? C * dv : 0);
-    total = gram + (exact_u ? pad4(C * C) : 0);
+    total = ck + pad4(C * tmax);
   }
 };
 
@@ -155,5 +149,6 @@ hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_
 hipError_t launch_eager(int kind, int dk, const EagerArgs& a, hipStream_t s);
 hipError_t launch_eager_accept(int32_t* slot, const int32_t* acc, int B, int T, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
+
 
 }  // namespace rs

@@ -40,46 +40,21 @@
 // nothing to fetch reads one fixed location instead of being skipped): the
 // next item then waits for its records without waiting for its checkpoint, and
 // for its checkpoint without waiting for the records requested after it.
-#include "device.hpp"
+#include "route.hpp"
 
 namespace rs {
-
-// A sequence's buffer pointers as one item reads them.
-struct SeqPtr {
-  int head, h, p;
-};
-
-// What one item does, from its sequence's pointers (the same in every
-// workgroup of the sequence).
-struct Route {
-  int T;        // drafts of this call (0 for flush)
-  bool corrupt; // pointers outside their invariant ranges
-  bool bad;     // corrupt, or a decode/verify call whose pending count is not T
-  bool fold;    // fold the committed records into the checkpoint first
-  bool work;    // anything to do for this item
-  bool outputs; // produce draft outputs
-  int R;        // staged records: committed [0, h), drafts [h, h + T)
-  int r0;       // first record replayed on top of the checkpoint
-};
-
-__device__ __forceinline__ Route route_of(const ReplayArgs& a, const SeqPtr& p) {
-  Route r;
-  r.T = (a.mode == kModeFlush) ? 0 : a.T;
-  r.corrupt = p.head < 0 || p.head >= a.C || p.h < 0 || p.h > a.L || p.p < 0 || p.p > a.C - a.L;
-  // decode/verify consume T pending drafts; the fused calls append them first (p = 0 on entry)
-  r.bad = r.corrupt || ((a.mode != kModeFlush) && (p.p != (a.fused ? 0 : r.T)));
-  r.fold = !r.bad && ((a.mode == kModeFlush) ? (p.h > 0) : (p.h + r.T > a.L));
-  r.work = !r.bad && (a.mode != kModeFlush || r.fold);
-  r.outputs = r.work && (a.mode != kModeFlush);
-  r.R = p.h + r.T;
-  r.r0 = r.fold ? p.h : 0;
-  return r;
-}
 
 // Which checkpoint copy an item reads: the bf16 one in the shared-bf16 mode,
 // and on the non-fold steps of the two-precision mode; fp32 otherwise.
 __device__ __forceinline__ bool reads_lp(int precision, bool fold) {
   return precision == REPLAYSSM_BF16_SHARED || (precision == REPLAYSSM_FP32_HP_BF16_LP && !fold);
+}
+
+// GDN with the two-precision checkpoint: a fold recomputes the folded records'
+// corrections from the fp32 checkpoint and their raw v.
+template <int KIND>
+__device__ __forceinline__ bool exact_fold(const Route& rt) {
+  return KIND == kKindGdnExact && rt.fold;
 }
 
 // Requests the checkpoint copy of `item` into S: the fp32 tiles, or the bf16
@@ -131,17 +106,12 @@ struct StageMap {
   }
 };
 
-__device__ __forceinline__ int ring_slot(int head, int r, int C) {
-  const int s = head + r;
-  return s >= C ? s - C : s;
-}
-
 // Source rows of one item: committed records from the ring; the drafts from
 // the ring too, or, in a fused call, straight from the caller's inputs.
 struct RowSrc {
   const float* rk;   // ring k rows of the head
   const float* rv;   // ring v rows
-  const float* rvraw;  // raw v rows (GDN, two-precision), else the same as rv
+  const float* rvraw;  // raw v rows (GDN with the two-precision checkpoint), else rv
   const float* ik;   // input k of draft 0 (fused), stride H * dk per draft
   const float* iv;   // input v of draft 0 (fused), stride H * dv per draft
   int64_t ia;        // index of draft 0 in the alpha / beta inputs, stride H per draft
@@ -183,9 +153,9 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
                                            : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck;
     rr.kb[j] = ld4(r < R ? src : a.ring_k);
   }
-  // a fold of the exact-correction kind stages the committed records' raw v (it
-  // recomputes their corrections); every other item stages the stored rows
-  const bool raw = KIND == kKindGdnExact && rt.fold;
+  // a fold with exact corrections stages the committed records' raw v instead of
+  // their stored corrections
+  const bool raw = exact_fold<KIND>(rt);
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
     const int r = m.rv0 + j * 16;
@@ -217,7 +187,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
                                               const StageMap& m, const RecRegs& rr) {
   constexpr int DK = NT * 16;
   constexpr bool GDN = kind_gdn(KIND);
-  const bool raw = KIND == kKindGdnExact && rt.fold;
+  const bool raw = exact_fold<KIND>(rt);
   const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
   const int b = item / H, hd = item - b * H;
   const RowSrc s = row_src<NT>(a, item, T);
@@ -250,8 +220,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     if (in) a.ring_alpha[s.bhC + slot] = al;
     if (GDN && (r >= p.h || raw)) {
       const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
-      if (r >= p.h) sm[lds.beta + (r - p.h)] = be;
-      if (raw) sm[lds.br + r] = be;
+      sm[lds.beta + r] = be;
       if (in) a.ring_beta[s.bhC + slot] = be;
     }
   }
@@ -280,8 +249,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     sm[lds.alpha + tid] = rr.al;
     if (fused && tid >= p.h) a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)] = rr.al;
     if (GDN && (tid >= p.h || raw)) {
-      if (tid >= p.h) sm[lds.beta + (tid - p.h)] = rr.be;
-      if (raw) sm[lds.br + tid] = rr.be;
+      sm[lds.beta + tid] = rr.be;
       if (fused && tid >= p.h) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
     }
   }
@@ -316,8 +284,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int hd = item - b * H;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
-  constexpr bool exact_u = KIND == kKindGdnExact;
-  const ReplayLds lds(C, DK, dv, TMAX, exact_u);
+  const ReplayLds lds(C, DK, dv, TMAX);
   const StageMap map(tid, nthr, LPR, dv);
 
   const int mode = a.mode;
@@ -452,67 +419,37 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // Gamma_h scales the checkpoint, gf_{j+1} weighs record j) are one
   // suffix-product scan per wavefront: lane t holds gf_t, and gf_hc = 1.
   // GDN with the two-precision checkpoint: the u stored with each committed
-  // record was computed from the bf16 copy. The fold recomputes them from the
-  // fp32 checkpoint in S and the records' raw v, so that the copy's rounding never
-  // reaches the checkpoint ("How it works": Gated DeltaNet and Two precisions).
-  // With D_j = prod_{m<j} alpha_m and g_ij = prod_{m=i+1..j-1} alpha_m, the state
-  // before record j applied to k_j is w_j = D_j (S_ck k_j) + sum_{i<j} g_ij
-  // (k_i . k_j) u_i, and u_j = beta_j (v_j - alpha_j w_j).
-  // The committed records' raw v and beta were staged in place of their stored
-  // corrections (LDS v rows, and lds.br) with the other rows.
-  auto exact_corrections = [&]() {
-    // Gram matrix of the committed keys, i < j
-    for (int id = tid; id < hc * hc; id += nthr) {
-      const int i = id / hc, j = id - i * hc;
-      if (i < j) {
-        float c = 0.f;
-        for (int n = 0; n < DK; n += 4)
-          c += dot4(ld4(sm + lds.k + i * lds.dks + n), ld4(sm + lds.k + j * lds.dks + n));
-        sm[lds.gram + i * C + j] = c;
-      }
-    }
-    // S_ck k_j on MFMA (16 records per block): lane l supplies A[l & 15][l >> 4] =
-    // k_{16 jb + (l & 15)}[16 nt + 4 (l >> 4) + c] and B[l >> 4][l & 15] = its own
-    // S[nt][c]; the block result gives lane l its row's values for records
-    // 16 jb + 4 (l >> 4) + i, i = 0..3.
-    for (int jb = 0; 16 * jb < hc; ++jb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int ja = 16 * jb + col;
-      const float* krow = sm + lds.k + (ja < hc ? ja : 0) * lds.dks + 4 * g;
+  // record was computed from the bf16 copy ("How it works": Gated DeltaNet and
+  // Two precisions). Such a fold instead applies the committed records one by one
+  // to the fp32 checkpoint in S, recomputing each correction from the state it
+  // follows: w = S k_j, u_j = beta_j (v_j - alpha_j w), S <- alpha_j S + u_j k_j^T
+  // (the staged v rows hold the raw v here). The bf16 rounding never reaches S.
+  auto exact_fold_state = [&]() {
+    for (int j = 0; j < hc; ++j) {
+      const float* kj = sm + lds.k + j * lds.dks + 4 * g;
+      float w = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) w += dot4(S[nt], ld4(kj + 16 * nt));
+      w = sum_groups(w);
+      const float al = sm[lds.alpha + j];
+      const float u = sm[lds.beta + j] * (sm[lds.v + j * lds.dvs + prow] - al * w);
+      // read k_j again rather than keep it in registers (a fresh address for the compiler)
+      const float* kj2 = kj;
+      __asm__ volatile("" : "+v"(kj2));
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ja < hc ? krow[16 * nt + c] : 0.f, S[nt][c], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * jb + 4 * g + i;
-        if (j < hc) sm[lds.y + j * dv + prow] = acc[i];
-      }
+      for (int nt = 0; nt < NT; ++nt) S[nt] = al * S[nt] + u * ld4(kj2 + 16 * nt);
     }
-    __syncthreads();
-    // the recurrence over the records, one thread per state row; u_j replaces
-    // v_j in the LDS row the fold reads
-    for (int p = tid; p < dv; p += nthr) {
-      float D = 1.f;
-      for (int j = 0; j < hc; ++j) {
-        float w = D * sm[lds.y + j * dv + p];
-        float gij = 1.f;
-        for (int i = j - 1; i >= 0; --i) {
-          w += gij * sm[lds.gram + i * C + j] * sm[lds.v + i * lds.dvs + p];
-          gij *= sm[lds.alpha + i];
-        }
-        const float al = sm[lds.alpha + j];
-        sm[lds.v + j * lds.dvs + p] = sm[lds.br + j] * (sm[lds.v + j * lds.dvs + p] - al * w);
-        D *= al;
-      }
-    }
-    __syncthreads();
   };
 
   auto fold_state = [&]() {
-    if constexpr (exact_u) exact_corrections();
+    if constexpr (KIND == kKindGdnExact) {
+      exact_fold_state();
+      if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, S);
+      if constexpr (NT >= 2) {
+        if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, S, prec == REPLAYSSM_BF16_SHARED);
+      }
+      return;
+    }
     float gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -591,7 +528,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 #pragma unroll
           for (int d = 0; d < i; ++d) w += gk[(hc + d + 1) * TMAX + i] * ck[(hc + d) * TMAX + i] * ud[d];
           const float al = sm[lds.alpha + hc + i];
-          const float be = sm[lds.beta + i];
+          const float be = sm[lds.beta + hc + i];
           ud[i] = be * (sv[(hc + i) * lds.dvs] - al * w);
           float o = oc[i];
 #pragma unroll
@@ -727,7 +664,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
 
 template <int KIND, int NT, int TMAX, bool FUSED>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND == kKindGdnExact);
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX);
   const int block = a.dv / 16 * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
