@@ -74,7 +74,7 @@ int check_config(const replayssm_config* c) {
     return fail(REPLAYSSM_ENOTSUP,
                 "the shared bf16 checkpoint is built for Mamba-2 only (GDN takes FP32 or "
                 "FP32_HP_BF16_LP)");
-  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max));
+  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max), exact_u(c));
   if (lds.total * 4 > rs::kMaxLdsBytes)
     return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
                 rs::kMaxLdsBytes);

@@ -104,17 +104,19 @@ struct EagerArgs {
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
 // wavefront reading one column of four consecutive rows hit distinct banks;
 // windows too long for that within kMaxLdsBytes use unpadded rows instead.
+// With gram (GDN with the two-precision checkpoint) one more block holds the
+// Gram matrix k_i . k_j of the staged records for the exact fold.
 constexpr int kMaxLdsBytes = 64 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, gram, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
-  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax) {
-    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv));
-    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv);
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, bool with_gram = false) {
+    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), with_gram);
+    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, with_gram);
   }
-  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride) {
+  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, bool with_gram) {
     dks = kstride;
     dvs = vstride;
     k = 0;
@@ -126,7 +128,8 @@ struct ReplayLds {
     gk = gq + pad4((C + 1) * tmax);
     cq = gk + pad4((C + 1) * tmax);
     ck = cq + pad4(C * tmax);
-    total = ck + pad4(C * tmax);
+    gram = ck + pad4(C * tmax);
+    total = gram + (with_gram ? pad4(C * C) : 0);
   }
 };
 

@@ -284,7 +284,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int hd = item - b * H;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
-  const ReplayLds lds(C, DK, dv, TMAX);
+  const ReplayLds lds(C, DK, dv, TMAX, KIND == kKindGdnExact);
   const StageMap map(tid, nthr, LPR, dv);
 
   const int mode = a.mode;
@@ -420,24 +420,79 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // suffix-product scan per wavefront: lane t holds gf_t, and gf_hc = 1.
   // GDN with the two-precision checkpoint: the u stored with each committed
   // record was computed from the bf16 copy ("How it works": Gated DeltaNet and
-  // Two precisions). Such a fold instead applies the committed records one by one
-  // to the fp32 checkpoint in S, recomputing each correction from the state it
-  // follows: w = S k_j, u_j = beta_j (v_j - alpha_j w), S <- alpha_j S + u_j k_j^T
-  // (the staged v rows hold the raw v here). The bf16 rounding never reaches S.
+  // Two precisions). Such a fold instead recomputes every correction from the
+  // fp32 checkpoint it follows (the staged v rows hold the raw v here), so the
+  // bf16 rounding never reaches S. Records go in blocks of four: with S the state
+  // before the block, D_j the decay from the block start to just before record j
+  // and g_ij = prod of alpha over (i, j),
+  //   w_j = D_j S k_j + sum_{i<j in block} g_ij (k_i . k_j) u_i,  u_j = beta_j (v_j - alpha_j w_j),
+  // then S <- D S + sum_i g_i u_i k_i^T over the block (D and g_i to its end) as one
+  // MFMA rank-4 step per tile. The four mat-vecs of a block are independent.
   auto exact_fold_state = [&]() {
-    for (int j = 0; j < hc; ++j) {
-      const float* kj = sm + lds.k + j * lds.dks + 4 * g;
-      float w = 0.f;
+    // Gram matrix of the staged committed keys, diagonal 16 x 16 blocks (the only
+    // pairs a block of four needs), by every wavefront (identical values): lane l
+    // supplies A[l & 15][l >> 4] = k_{16 jb + (l & 15)}[n] and B[l >> 4][l & 15] =
+    // k_{16 jb + (l & 15)}[n] for n = 16 c + 4 (l >> 4) + e; the result gives lane l
+    // entry (16 jb + 4 (l >> 4) + r, 16 jb + (l & 15)), r = 0..3.
+    for (int jb = 0; 16 * jb < hc; ++jb) {
+      const int ja = 16 * jb + col;
+      const float* krow = sm + lds.k + (ja < hc ? ja : 0) * lds.dks + 4 * g;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) w += dot4(S[nt], ld4(kj + 16 * nt));
-      w = sum_groups(w);
-      const float al = sm[lds.alpha + j];
-      const float u = sm[lds.beta + j] * (sm[lds.v + j * lds.dvs + prow] - al * w);
-      // read k_j again rather than keep it in registers (a fresh address for the compiler)
-      const float* kj2 = kj;
-      __asm__ volatile("" : "+v"(kj2));
+      for (int c = 0; c < NT; ++c) {
+        const f32x4 f = ja < hc ? ld4(krow + 16 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[nt] = al * S[nt] + u * ld4(kj2 + 16 * nt);
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], f[e], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jb + 4 * g + r;
+        if (j < hc && ja < hc) sm[lds.gram + ja * C + j] = acc[r];
+      }
+    }
+    for (int j0 = 0; j0 < hc; j0 += 4) {
+      const int nb = hc - j0 < 4 ? hc - j0 : 4;
+      float w0[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float* kj = sm + lds.k + (jj < nb ? j0 + jj : 0) * lds.dks + 4 * g;
+        float part = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) part += dot4(S[nt], ld4(kj + 16 * nt));
+        w0[jj] = part;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w0[jj] = sum_groups(w0[jj]);
+      float u[4];
+      float D = 1.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        u[jj] = 0.f;
+        if (jj < nb) {
+          const int j = j0 + jj;
+          float w = D * w0[jj];
+          float gij = 1.f;
+#pragma unroll
+          for (int ii = jj - 1; ii >= 0; --ii) {
+            w += gij * sm[lds.gram + (j0 + ii) * C + j] * u[ii];
+            gij *= sm[lds.alpha + j0 + ii];
+          }
+          const float al = sm[lds.alpha + j];
+          u[jj] = sm[lds.beta + j] * (sm[lds.v + j * lds.dvs + prow] - al * w);
+          D *= al;
+        }
+      }
+      // decay of record j0 + g from itself to the end of the block
+      float ge = 1.f;
+      for (int m = j0 + g + 1; m < j0 + nb; ++m) ge *= sm[lds.alpha + m];
+      const bool vj = g < nb;
+      const float bval = vj ? ge * (g == 0 ? u[0] : g == 1 ? u[1] : g == 2 ? u[2] : u[3]) : 0.f;
+      const float* krow = sm + lds.k + (vj ? j0 + g : 0) * lds.dks + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        S[nt] *= D;
+        S[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vj ? krow[nt * 16] : 0.f, bval, S[nt], 0, 0, 0);
+      }
     }
   };
 
@@ -664,7 +719,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
 
 template <int KIND, int NT, int TMAX, bool FUSED>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX);
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND == kKindGdnExact);
   const int block = a.dv / 16 * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
