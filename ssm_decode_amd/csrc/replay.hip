@@ -384,30 +384,23 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     }
   }
   if (outputs) {
+    // one draft at a time, q_i (and k_i) re-read from LDS per pass: a register
+    // copy of every draft's vectors would cost 4 (GDN: 8) registers per draft
     const int sub = lane / LPR, li = lane % LPR;
-    f32x4 qf[TMAX], kf[TMAX];
-#pragma unroll
-    for (int i = 0; i < TMAX; ++i) {
-      qf[i] = ld4(sm + lds.q + i * DK + 4 * li);
-      kf[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (GDN && i < T) kf[i] = ld4(sm + lds.k + (hc + i) * lds.dks + 4 * li);
-    }
     for (int base = r0 + wave * RPI; base < R; base += W * RPI) {
       const int r = base + sub;
       const bool valid = r < R;
       f32x4 kr = f32x4{0.f, 0.f, 0.f, 0.f};
       if (valid) kr = ld4(sm + lds.k + r * lds.dks + 4 * li);
-      float dq[TMAX], dkk[TMAX];
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
-        dq[i] = sum_width<LPR>(dot4(kr, qf[i]));
-        dkk[i] = GDN ? sum_width<LPR>(dot4(kr, kf[i])) : 0.f;
-      }
-      if (valid && li == 0) {
-#pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-          sm[lds.cq + r * TMAX + i] = dq[i];
-          if (GDN) sm[lds.ck + r * TMAX + i] = dkk[i];
+        if (i < T) {
+          const float dq = sum_width<LPR>(dot4(kr, ld4(sm + lds.q + i * DK + 4 * li)));
+          if (valid && li == 0) sm[lds.cq + r * TMAX + i] = dq;
+          if constexpr (GDN) {
+            const float dkk = sum_width<LPR>(dot4(kr, ld4(sm + lds.k + (hc + i) * lds.dks + 4 * li)));
+            if (valid && li == 0) sm[lds.ck + r * TMAX + i] = dkk;
+          }
         }
       }
     }
