@@ -35,11 +35,13 @@
 // records (into registers), and as soon as this item's mat-vecs have consumed
 // S, the next item's checkpoint (into S, in the precision that item's route
 // reads). Both stream in while this item computes. Vector memory operations
-// complete in order and the compiler waits on them by count, so every path
-// through an item issues the same loads in the same order (a load that has
-// nothing to fetch reads one fixed location instead of being skipped): the
-// next item then waits for its records without waiting for its checkpoint, and
-// for its checkpoint without waiting for the records requested after it.
+// complete in order and the compiler waits on them by count, taking the
+// smallest count over every control-flow path; so every path through an item
+// issues the same record loads in the same order (a load that has nothing to
+// fetch reads one fixed location instead of being skipped) and makes the
+// checkpoint request at one program point: the next item then waits for its
+// records without waiting for its checkpoint, and for its checkpoint without
+// waiting for the records requested after it.
 #include "route.hpp"
 
 namespace rs {
@@ -58,12 +60,11 @@ __device__ __forceinline__ bool exact_fold(const Route& rt) {
 }
 
 // Requests the checkpoint copy of `item` into S: the fp32 tiles, or the bf16
-// copy's raw 16-byte chunks in S[0, NT/2) (widened in place when used). Both
-// forms are the same NT loads per lane with computed addresses, no branch: in
-// the bf16 form the loads into S[NT/2, NT) read distinct 16-byte chunks at the
-// start of the array (widening overwrites them), and with valid false (no
-// item, or an item with nothing to do) all of them read the array's first
-// bytes.
+// copy's raw 16-byte chunks in S[0, NT/2) (widened in place when used), with
+// computed addresses and no branch; with valid false (no item, or an item with
+// nothing to do) every load reads the array's first bytes. (The bf16 form issues
+// half the loads of the fp32 one; padding it to the same count, which keeps the
+// compiler's waits after it exact, measured slower than the waits it saves.)
 template <int NT>
 __device__ __forceinline__ void prefetch_ckpt(const ReplayArgs& a, int item, bool fold, bool valid, int wave,
                                               int lane, f32x4 (&S)[NT]) {
@@ -75,20 +76,24 @@ __device__ __forceinline__ void prefetch_ckpt(const ReplayArgs& a, int item, boo
   const int step = valid ? 1024 : 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const bool pad = lp && nt >= NT / 2;
-    const char* src = pad ? base + nt * 16 : base + start + nt * step;
+    if (lp && nt >= NT / 2) continue;
+    const char* src = base + start + nt * step;
     S[nt] = __builtin_bit_cast(f32x4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)));
   }
 }
 
-// One item's ring rows while they are in flight: up to kRecK k-row and kRecV
-// v-row passes per thread (a pass is nthr / (dk / 4) k rows or 16 v rows), the
-// thread's float4 of the drafts' q, and its alpha / beta. With dk = 128 and
-// dv >= 64 this covers the L <= 16 rows of every non-fold item; the extra rows
-// of a fold item (up to L + T) go through the tail loop of store_records.
-constexpr int kRecK = 2, kRecV = 1;
+// One item's ring rows while they are in flight: up to K k-row and V v-row
+// passes per thread (a pass is nthr / (dk / 4) k rows or 16 v rows), the
+// thread's float4 of the drafts' q, and its alpha / beta. Rows beyond the
+// passes go through the tail loop of store_records, which waits for each row.
+// With dk = 128 and dv >= 64 two k passes and one v pass cover 16 rows. (Every
+// pass is issued whether or not its rows exist, which keeps the compiler's
+// memory waits exact but costs a request per pass: three k and two v passes
+// for the verify kernels measured slower than the tail loop they save.)
+template <int TMAX>
 struct RecRegs {
-  f32x4 kb[kRecK], vb[kRecV], qv;
+  static constexpr int K = 2, V = 1;
+  f32x4 kb[K], vb[V], qv;
   float al, be;
 };
 
@@ -135,9 +140,10 @@ __device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) 
   return s;
 }
 
-template <int KIND, int NT, bool FUSED>
+template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, const SeqPtr& p, const Route& rt,
-                                             bool valid, int tid, const StageMap& m, RecRegs& rr) {
+                                             bool valid, int tid, const StageMap& m, RecRegs<TMAX>& rr) {
+  constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
   constexpr int DK = NT * 16;
   // Every load is issued; one with nothing to fetch reads the first element of a
   // ring array (always allocated: q and the inputs are NULL in a flush call).
@@ -184,7 +190,8 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
 template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds, int item,
                                               const SeqPtr& p, const Route& rt, int tid, int nthr,
-                                              const StageMap& m, const RecRegs& rr) {
+                                              const StageMap& m, const RecRegs<TMAX>& rr) {
+  constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
   constexpr int DK = NT * 16;
   constexpr bool GDN = kind_gdn(KIND);
   const bool raw = exact_fold<KIND>(rt);
@@ -261,7 +268,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
 // checkpoint copy. Ends with a workgroup barrier after its last LDS read.
 template <int KIND, int NT, int TMAX, bool FUSED>
 __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const int item, const SeqPtr ptr,
-                                            const Route rt, f32x4 (&S)[NT], RecRegs& rr, const int next,
+                                            const Route rt, f32x4 (&S)[NT], RecRegs<TMAX>& rr, const int next,
                                             const SeqPtr nptr, const Route nrt) {
   constexpr int DK = NT * 16;
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
@@ -305,7 +312,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 
   // ---- the next item's ring rows: requested now, waited for by the next item
   const bool more = next < a.B * a.H;
-  load_records<KIND, NT, FUSED>(a, next, nptr, nrt, more, tid, map, rr);
+  load_records<KIND, NT, TMAX, FUSED>(a, next, nptr, nrt, more, tid, map, rr);
   // the next item's checkpoint copy, requested once S is free (same loads on every path). The
   // empty asm marks every S register as read here, on every path: no load into S can still be
   // pending when S is reloaded, so the compiler's waits before the reload stay at zero.
@@ -682,10 +689,10 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   const bool any = (int)blockIdx.x < items;
   if (!any) rt.work = false;
   f32x4 S[NT];
-  RecRegs rr;
+  RecRegs<TMAX> rr;
   {
     const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
-    load_records<KIND, NT, FUSED>(a, blockIdx.x, ptr, rt, any, threadIdx.x, map, rr);
+    load_records<KIND, NT, TMAX, FUSED>(a, blockIdx.x, ptr, rt, any, threadIdx.x, map, rr);
   }
   prefetch_ckpt<NT>(a, blockIdx.x, rt.fold, any && rt.work, wave, lane, S);
   for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) {
