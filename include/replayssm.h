@@ -57,6 +57,8 @@ extern "C" {
 #define REPLAYSSM_DEVERR_PENDING 2         /* decode/verify: p != T; sequence skipped     */
 #define REPLAYSSM_DEVERR_ACCEPT 4          /* accept: a < 0, a > p or h + a > L; clamped  */
 #define REPLAYSSM_DEVERR_CORRUPT 8         /* head/h/p out of range; sequence skipped     */
+#define REPLAYSSM_DEVERR_STALE 16          /* snapshot of a sequence with unfolded records */
+#define REPLAYSSM_DEVERR_INDEX 32          /* sequence index outside 0..B-1; skipped       */
 
 /* ---- configuration ------------------------------------------------------ */
 enum replayssm_kind {
@@ -227,6 +229,34 @@ int replayssm_accept(const replayssm_config* cfg, const replayssm_state* st,
  * folded += h, h = 0. Pending drafts are kept. Sequences with h = 0 are left
  * alone. Afterwards the checkpoint alone is the state at position `folded`. */
 int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void* stream);
+
+/* ---- prefix states -------------------------------------------------------
+ * The checkpoint alone is a sequence's state only once its committed records are
+ * folded; until then it trails them (the staleness raised about prefix caching in
+ * the replies of the thread on "ReplaySSM"). These calls let a state be shared
+ * between sequences, e.g. a cached prompt prefix: fold, copy it out, start other
+ * sequences from it. */
+
+/* replayssm_flush for the sequences with select[b] != 0 only (select: [B] int32,
+ * device memory); the others keep their checkpoints and pointers. */
+int replayssm_flush_selected(const replayssm_config* cfg, const replayssm_state* st,
+                             const int32_t* select, void* stream);
+
+/* Copies the checkpoints of sequences seqs[0..n) (device int32) to dst
+ * [n][H][dv][dk] fp32, logical layout (from the fp32 copy; from the bf16 one in
+ * BF16_SHARED mode). The state is the sequence's at position `folded` only when
+ * h = 0: a sequence with unfolded records is copied anyway and sets
+ * REPLAYSSM_DEVERR_STALE (fold it first with replayssm_flush_selected). Indices
+ * outside 0..B-1 are skipped and set REPLAYSSM_DEVERR_INDEX. n >= 0. */
+int replayssm_snapshot(const replayssm_config* cfg, const replayssm_state* st, int n,
+                       const int32_t* seqs, float* dst, void* stream);
+
+/* Starts sequences seqs[0..n) from the states src [n][H][dv][dk] fp32: their
+ * checkpoints (every copy the mode keeps; bf16 by round-to-nearest-even) are set
+ * from src and their buffers emptied (head = h = p = 0, folded = 0). Indices
+ * outside 0..B-1 are skipped and set REPLAYSSM_DEVERR_INDEX. n >= 0. */
+int replayssm_restore(const replayssm_config* cfg, const replayssm_state* st, int n,
+                      const int32_t* seqs, const float* src, void* stream);
 
 /* The same two calls fused with the append that precedes them, in one launch
  * (the new records are read from the inputs and written to the ring by the

@@ -27,7 +27,7 @@ PRECISIONS = {"fp32": FP32, "fp32_hp_bf16_lp": FP32_HP_BF16_LP, "bf16_shared": B
 KINDS = {"mamba2": MAMBA2, "gdn": GDN}
 
 OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
-DEVERR_APPEND_OVERFLOW, DEVERR_PENDING, DEVERR_ACCEPT, DEVERR_CORRUPT = 1, 2, 4, 8
+DEVERR_APPEND_OVERFLOW, DEVERR_PENDING, DEVERR_ACCEPT, DEVERR_CORRUPT, DEVERR_STALE, DEVERR_INDEX = 1, 2, 4, 8, 16, 32
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -77,6 +77,9 @@ SIGNATURES = {
     "replayssm_eager_verify": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "replayssm_eager_accept": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp],
     "replayssm_probe_read": [_vp, ctypes.c_int64, _vp, _vp],
+    "replayssm_flush_selected": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp],
+    "replayssm_snapshot": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
+    "replayssm_restore": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
 }
 STRING_FUNCTIONS = {"replayssm_status_string": [ctypes.c_int], "replayssm_last_error": []}
 
@@ -217,6 +220,21 @@ def eager_verify(cfg, pool, slot, T, alpha, k, v, beta, q, out, stream=None):
 def eager_accept(cfg, slot, accepted, T, stream=None):
     _check(lib().replayssm_eager_accept(ctypes.byref(cfg), _i32t(slot), _i32t(accepted), int(T), _s(stream)),
            "eager_accept")
+
+
+def flush_selected(cfg, st, select, stream=None):
+    _check(lib().replayssm_flush_selected(ctypes.byref(cfg), ctypes.byref(st), _i32t(select), _s(stream)),
+           "flush_selected")
+
+
+def snapshot(cfg, st, seqs, dst, stream=None):
+    _check(lib().replayssm_snapshot(ctypes.byref(cfg), ctypes.byref(st), int(seqs.numel()), _i32t(seqs), _f32(dst),
+                                    _s(stream)), "snapshot")
+
+
+def restore(cfg, st, seqs, src, stream=None):
+    _check(lib().replayssm_restore(ctypes.byref(cfg), ctypes.byref(st), int(seqs.numel()), _i32t(seqs), _f32(src),
+                                   _s(stream)), "restore")
 
 
 def probe_read(src, sink, stream=None):

@@ -328,6 +328,45 @@ int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void
   return hip_result(replay(cfg, 1, a, as_stream(stream)), "flush");
 }
 
+int replayssm_flush_selected(const replayssm_config* cfg, const replayssm_state* st,
+                             const int32_t* select, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  NEED(select);
+  rs::ReplayArgs a = replay_args(cfg, st, 0, rs::kModeFlush, nullptr, nullptr);
+  a.select = select;
+  return hip_result(replay(cfg, 1, a, as_stream(stream)), "flush_selected");
+}
+
+int replayssm_snapshot(const replayssm_config* cfg, const replayssm_state* st, int n,
+                       const int32_t* seqs, float* dst, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  if (n < 0) return fail(REPLAYSSM_EINVAL, "n=%d < 0", n);
+  if (n == 0) return REPLAYSSM_OK;
+  NEED(seqs);
+  NEED(dst);
+  const float* hp = cfg->precision == REPLAYSSM_BF16_SHARED ? nullptr : st->hp;
+  return hip_result(rs::launch_snapshot(hp, st->lp, st->h, st->err, seqs, n, dst, cfg->B, cfg->H, cfg->dv,
+                                        cfg->dk, as_stream(stream)),
+                    "snapshot");
+}
+
+int replayssm_restore(const replayssm_config* cfg, const replayssm_state* st, int n,
+                      const int32_t* seqs, const float* src, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  if (n < 0) return fail(REPLAYSSM_EINVAL, "n=%d < 0", n);
+  if (n == 0) return REPLAYSSM_OK;
+  NEED(seqs);
+  NEED(src);
+  float* hp = cfg->precision == REPLAYSSM_BF16_SHARED ? nullptr : st->hp;
+  uint16_t* lp = cfg->precision == REPLAYSSM_FP32 ? nullptr : st->lp;
+  return hip_result(rs::launch_restore(hp, lp, st->head, st->h, st->p, st->folded, st->err, seqs, n, src, cfg->B,
+                                       cfg->H, cfg->dv, cfg->dk, as_stream(stream)),
+                    "restore");
+}
+
 int replayssm_eager_step(const replayssm_config* cfg, float* S, const float* alpha, const float* k,
                          const float* v, const float* beta, const float* q, float* out,
                          void* stream) {

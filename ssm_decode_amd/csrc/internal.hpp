@@ -55,6 +55,7 @@ struct ReplayArgs {
   int32_t* arrive;
   int32_t* err;
   float* ring_vraw;  // GDN two-precision: raw v of every record, for the fold
+  const int32_t* select;  // flush only: [B] nonzero = fold this sequence; NULL = all
   const float* q;  // [B][T][H][dk]
   float* out;      // [B][T][H][dv]
   // fused append: the T new records come from these inputs (and are written to
@@ -149,6 +150,13 @@ hipError_t launch_pack(const float* src, float* hp, uint16_t* lp, int64_t nheads
                        hipStream_t s);
 hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_t nheads, int dv,
                          int dk, hipStream_t s);
+// Prefix states: the listed sequences' checkpoints out to / in from the logical layout.
+hipError_t launch_snapshot(const float* hp, const uint16_t* lp, const int32_t* h, int32_t* err,
+                           const int32_t* seqs, int n, float* dst, int B, int H, int dv, int dk,
+                           hipStream_t s);
+hipError_t launch_restore(float* hp, uint16_t* lp, int32_t* head, int32_t* h, int32_t* p, int64_t* folded,
+                          int32_t* err, const int32_t* seqs, int n, const float* src, int B, int H, int dv,
+                          int dk, hipStream_t s);
 hipError_t launch_eager(int kind, int dk, const EagerArgs& a, hipStream_t s);
 hipError_t launch_eager_accept(int32_t* slot, const int32_t* acc, int B, int T, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);

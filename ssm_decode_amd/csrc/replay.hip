@@ -632,6 +632,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 // replay_kernel), all its threads striding over the sequences.
 __device__ __forceinline__ void commit_pointers(const ReplayArgs& a, int tid, int nthr) {
   for (int b = tid; b < a.B; b += nthr) {
+    if (a.select && a.select[b] == 0) continue;
     const SeqPtr p{a.head[b], a.h[b], a.p[b]};
     const Route rt = route_of(a, p);
     if (rt.bad) {
@@ -673,6 +674,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
       ph = a.head[bb];
       phc = a.h[bb];
       pp = a.p[bb];
+      if (a.select && a.select[bb] == 0) phc = 0;  // a selective flush leaves it alone
     }
     // Wait for them here, once per batch. Left pending, they would be the
     // newest loads on one path into the next item and the oldest on the other,

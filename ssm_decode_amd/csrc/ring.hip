@@ -217,6 +217,101 @@ hipError_t launch_pack(const float* src, float* hp, uint16_t* lp, int64_t nheads
   return hipGetLastError();
 }
 
+// Prefix states. A cached prefix is shared between sequences as a plain state:
+// the checkpoint of a sequence whose committed records are all folded (the
+// checkpoint alone trails the tokens by the unfolded records, the staleness
+// raised in the thread's replies on prefix caching). One thread per (listed
+// sequence, head, tile, lane), as in pack/unpack; indices outside 0..B-1 are
+// skipped and flagged.
+__global__ void __launch_bounds__(256) snapshot_kernel(const float* hp, const uint16_t* lp, const int32_t* h,
+                                                       int32_t* err, const int32_t* seqs, int n, float* dst,
+                                                       int B, int H, int dv, int dk) {
+  const int NT = dk >> 4, PT = dv >> 4;
+  const int64_t per_seq = (int64_t)H * PT * NT * 64;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)n * per_seq) return;
+  const int i = (int)(gid / per_seq);
+  const int b = seqs[i];
+  const int64_t rest = gid - (int64_t)i * per_seq;
+  if (b < 0 || b >= B) {
+    if (rest == 0) atomicOr(err, REPLAYSSM_DEVERR_INDEX);
+    return;
+  }
+  if (rest == 0 && h[b] != 0) atomicOr(err, REPLAYSSM_DEVERR_STALE);
+  const int lane = (int)(rest & 63);
+  const int64_t t = rest >> 6;
+  const int tile = (int)(t % (PT * NT));
+  const int hd = (int)(t / (PT * NT));
+  const int pt = tile / NT, nt = tile - pt * NT;
+  const int pr = 16 * pt + (lane & 15), nc = 16 * nt + 4 * (lane >> 4);
+  const int64_t src_base = ((int64_t)b * H + hd) * dv * dk;
+  f32x4 x;
+  if (hp) {
+    x = ld4(hp + src_base + tile * 256 + lane * 4);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(lp + src_base + (pt * (NT / 2) + nt / 2) * 512 + lane * 8 +
+                                                     (nt & 1) * 4);
+    x = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+  }
+  st4(dst + ((int64_t)i * H + hd) * dv * dk + (int64_t)pr * dk + nc, x);
+}
+
+__global__ void __launch_bounds__(256) restore_kernel(float* hp, uint16_t* lp, int32_t* head, int32_t* h,
+                                                      int32_t* p, int64_t* folded, int32_t* err,
+                                                      const int32_t* seqs, int n, const float* src, int B, int H,
+                                                      int dv, int dk) {
+  const int NT = dk >> 4, PT = dv >> 4;
+  const int64_t per_seq = (int64_t)H * PT * NT * 64;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)n * per_seq) return;
+  const int i = (int)(gid / per_seq);
+  const int b = seqs[i];
+  const int64_t rest = gid - (int64_t)i * per_seq;
+  if (b < 0 || b >= B) {
+    if (rest == 0) atomicOr(err, REPLAYSSM_DEVERR_INDEX);
+    return;
+  }
+  if (rest == 0) {
+    head[b] = 0;
+    h[b] = 0;
+    p[b] = 0;
+    folded[b] = 0;
+  }
+  const int lane = (int)(rest & 63);
+  const int64_t t = rest >> 6;
+  const int tile = (int)(t % (PT * NT));
+  const int hd = (int)(t / (PT * NT));
+  const int pt = tile / NT, nt = tile - pt * NT;
+  const int pr = 16 * pt + (lane & 15), nc = 16 * nt + 4 * (lane >> 4);
+  const f32x4 x = ld4(src + ((int64_t)i * H + hd) * dv * dk + (int64_t)pr * dk + nc);
+  const int64_t dst_base = ((int64_t)b * H + hd) * dv * dk;
+  if (hp) st4(hp + dst_base + tile * 256 + lane * 4, x);
+  if (lp) {
+    uint2* d = reinterpret_cast<uint2*>(lp + dst_base + (pt * (NT / 2) + nt / 2) * 512 + lane * 8 + (nt & 1) * 4);
+    *d = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  }
+}
+
+hipError_t launch_snapshot(const float* hp, const uint16_t* lp, const int32_t* h, int32_t* err,
+                           const int32_t* seqs, int n, float* dst, int B, int H, int dv, int dk,
+                           hipStream_t s) {
+  const int64_t threads = (int64_t)n * H * (dv / 16) * (dk / 16) * 64;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(snapshot_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, hp, lp, h, err,
+                     seqs, n, dst, B, H, dv, dk);
+  return hipGetLastError();
+}
+
+hipError_t launch_restore(float* hp, uint16_t* lp, int32_t* head, int32_t* h, int32_t* p, int64_t* folded,
+                          int32_t* err, const int32_t* seqs, int n, const float* src, int B, int H, int dv,
+                          int dk, hipStream_t s) {
+  const int64_t threads = (int64_t)n * H * (dv / 16) * (dk / 16) * 64;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(restore_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, hp, lp, head, h, p,
+                     folded, err, seqs, n, src, B, H, dv, dk);
+  return hipGetLastError();
+}
+
 hipError_t launch_unpack(const float* hp, const uint16_t* lp, float* dst, int64_t nheads, int dv,
                          int dk, hipStream_t s) {
   const int64_t threads = nheads * (dv / 16) * (dk / 16) * 64;

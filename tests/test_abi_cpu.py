@@ -119,6 +119,11 @@ def test_calls_reject_bad_arguments_before_enqueueing(rs):
     assert L.replayssm_pack_state(ctypes.byref(cfg), fake, None, None, None) == rs.EINVAL
     assert L.replayssm_unpack_state(ctypes.byref(cfg), None, None, fake, None) == rs.EINVAL
     assert L.replayssm_read_error(None, None, None) == rs.EINVAL
+    assert L.replayssm_flush_selected(ctypes.byref(cfg), ctypes.byref(st_ok), None, None) == rs.EINVAL
+    assert L.replayssm_snapshot(ctypes.byref(cfg), ctypes.byref(st_ok), -1, fake, fake, None) == rs.EINVAL
+    assert L.replayssm_snapshot(ctypes.byref(cfg), ctypes.byref(st_ok), 0, None, None, None) == rs.OK  # nothing to do
+    assert L.replayssm_snapshot(ctypes.byref(cfg), ctypes.byref(st_ok), 2, None, fake, None) == rs.EINVAL
+    assert L.replayssm_restore(ctypes.byref(cfg), ctypes.byref(st_ok), 2, fake, None, None) == rs.EINVAL
     assert L.replayssm_probe_read(None, 1024, fake, None) == rs.EINVAL
     assert L.replayssm_probe_read(fake, 1000, fake, None) == rs.EINVAL
     assert "multiple of 16" in rs.last_error()
