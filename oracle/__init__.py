@@ -45,6 +45,8 @@ def lib():
         L.oracle_mamba2_round_f32.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_gdn_round_f64.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_gdn_round_f32.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        L.oracle_kda_round_f64.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+        L.oracle_kda_round_f32.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -102,5 +104,26 @@ def gdn_round(S, alpha, beta, k, v, q, acc, precision: str = "f64"):
     out = np.empty((nh, T, P), dt)
     u = np.empty((nh, T, P), dt)
     fn = lib().oracle_gdn_round_f64 if precision == "f64" else lib().oracle_gdn_round_f32
+    fn(nh, P, N, T, S.ctypes.data, pal, pbe, pk, pv, pq, pac, out.ctypes.data, u.ctypes.data)
+    return out, u
+
+
+def kda_round(S, alpha, beta, k, v, q, acc, precision: str = "f64"):
+    """One round over nh heads of Kimi Delta Attention (per-channel gate alpha [nh,T,N]).
+    Returns (out, u), each [nh,T,P]; u_t = beta_t (v_t - S_{t-1} (alpha_t * k_t))."""
+    dt = np.float64 if precision == "f64" else np.float32
+    assert S.dtype == dt and S.flags.c_contiguous
+    nh, P, N = S.shape
+    T = beta.shape[1]
+    al, pal = _c(alpha, np.float32)
+    be, pbe = _c(beta, np.float32)
+    kk, pk = _c(k, np.float32)
+    vv, pv = _c(v, np.float32)
+    qq, pq = _c(q, np.float32)
+    ac, pac = _c(acc, np.int32)
+    assert al.shape == (nh, T, N) and kk.shape == (nh, T, N) and qq.shape == (nh, T, N) and vv.shape == (nh, T, P)
+    out = np.empty((nh, T, P), dt)
+    u = np.empty((nh, T, P), dt)
+    fn = lib().oracle_kda_round_f64 if precision == "f64" else lib().oracle_kda_round_f32
     fn(nh, P, N, T, S.ctypes.data, pal, pbe, pk, pv, pq, pac, out.ctypes.data, u.ctypes.data)
     return out, u

@@ -14,7 +14,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import gdn_round, mamba2_round
+from . import gdn_round, kda_round, mamba2_round
 from .pointer_model import PointerModel
 
 
@@ -48,7 +48,7 @@ class OracleSession:
         slots = self.pm.append(T)
         new = {"alpha": np.asarray(alpha, np.float32), "k": np.asarray(k, np.float32),
                "v": np.asarray(v, np.float32)}
-        if self.kind == "gdn":
+        if self.kind in ("gdn", "kda"):
             new["beta"] = np.asarray(beta, np.float32)
         if self.pending is None:
             self.pending = new
@@ -60,6 +60,8 @@ class OracleSession:
         pd = self.pending
         if self.kind == "mamba2":
             return mamba2_round(self.S, pd["alpha"], pd["k"], pd["v"], q, acc_heads, self.precision), None
+        if self.kind == "kda":
+            return kda_round(self.S, pd["alpha"], pd["beta"], pd["k"], pd["v"], q, acc_heads, self.precision)
         return gdn_round(self.S, pd["alpha"], pd["beta"], pd["k"], pd["v"], q, acc_heads, self.precision)
 
     def _take_checkpoint(self, folds: Sequence[bool]) -> None:

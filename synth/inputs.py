@@ -9,12 +9,15 @@ Mamba-2
 Gated DeltaNet
   k, q = g / ||g||_2 with g ~ N(0, I)  (independently for k and q)
   v ~ N(0, 1), beta = sigmoid(N(0, 1)), alpha = exp(-softplus(N(0, 1)))
+Kimi Delta Attention
+  as Gated DeltaNet, with one gate per key channel: alpha [.., N], each entry
+  exp(-softplus(N(0, 1))) independently
 Initial checkpoint: zero, or N(0, sigma^2) entries.
 Acceptance lengths (speculative rounds): uniform on {0, ..., T} per sequence.
 Supplementary "slow" decay: alpha ~ U[0.9, 1) instead of the recipe above.
 
 Array layouts (all float32, C-contiguous):
-  alpha, beta : [B, T, H]
+  alpha, beta : [B, T, H]            (KDA: alpha [B, T, H, N])
   k, q        : [B, T, H, N]       (N = d_state for Mamba-2, d_k for GDN)
   v           : [B, T, H, P]       (P = head dim for Mamba-2, d_v for GDN)
   S0          : [B, H, P, N]       (logical state layout, row p, column n)
@@ -38,7 +41,7 @@ _F_ALPHA_DT, _F_ALPHA_A, _F_K, _F_V, _F_Q, _F_BETA, _F_S0, _F_ACC = range(8)
 
 @dataclass(frozen=True)
 class LayerShape:
-    kind: str  # "mamba2" | "gdn"
+    kind: str  # "mamba2" | "gdn" | "kda"
     B: int
     H: int
     P: int  # Mamba-2 head dim / GDN d_v
@@ -83,6 +86,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(4, "mamba2_2prec_b256", LayerShape("mamba2", 256, 128, 64, 128),
                  L=16, T=4, steps=1024, s0_sigma=0.1, precision="fp32_hp_bf16_lp",
                  extra={"batch_sweep": (1, 32, 256, 512)}),
+        Workload(5, "kda_decode_b256", LayerShape("kda", 256, 32, 128, 128),
+                 L=16, T=1, steps=512, s0_sigma=0.1, extra={"spec_T": 4}),
     ]
 }
 
@@ -105,14 +110,15 @@ def host_step(seed: int, wid: int, step: int, shape: LayerShape, T: int,
     """Inputs of T tokens (or T drafts) for every (sequence, head) of one step."""
     B, H, P, N = shape.B, shape.H, shape.P, shape.N
     out: Dict[str, np.ndarray] = {}
+    ashape = (B, T, H, N) if shape.kind == "kda" else (B, T, H)
     if decay == "slow":
-        out["alpha"] = _rng(seed, wid, step, _F_ALPHA_DT).uniform(0.9, 1.0, (B, T, H)).astype(np.float32)
+        out["alpha"] = _rng(seed, wid, step, _F_ALPHA_DT).uniform(0.9, 1.0, ashape).astype(np.float32)
     elif shape.kind == "mamba2":
         dt = _rng(seed, wid, step, _F_ALPHA_DT).standard_normal((B, T, H))
         a = _rng(seed, wid, step, _F_ALPHA_A).uniform(0.5, 2.0, (B, T, H))
         out["alpha"] = np.exp(-_softplus(dt) * a).astype(np.float32)
     else:
-        g = _rng(seed, wid, step, _F_ALPHA_DT).standard_normal((B, T, H))
+        g = _rng(seed, wid, step, _F_ALPHA_DT).standard_normal(ashape)
         out["alpha"] = np.exp(-_softplus(g)).astype(np.float32)
     if shape.kind == "mamba2":
         sc = 1.0 / np.sqrt(N)
@@ -161,14 +167,15 @@ def device_step(seed: int, wid: int, step: int, shape: LayerShape, T: int, devic
 
     B, H, P, N = shape.B, shape.H, shape.P, shape.N
     f32 = torch.float32
+    ashape = (B, T, H, N) if shape.kind == "kda" else (B, T, H)
     if out is None:
         out = {
-            "alpha": torch.empty((B, T, H), dtype=f32, device=device),
+            "alpha": torch.empty(ashape, dtype=f32, device=device),
             "k": torch.empty((B, T, H, N), dtype=f32, device=device),
             "q": torch.empty((B, T, H, N), dtype=f32, device=device),
             "v": torch.empty((B, T, H, P), dtype=f32, device=device),
         }
-        if shape.kind == "gdn":
+        if shape.kind in ("gdn", "kda"):
             out["beta"] = torch.empty((B, T, H), dtype=f32, device=device)
     if decay == "slow":
         out["alpha"].uniform_(0.9, 1.0, generator=_gen(device, seed, wid, step, _F_ALPHA_DT))
@@ -179,7 +186,7 @@ def device_step(seed: int, wid: int, step: int, shape: LayerShape, T: int, devic
             0.5, 2.0, generator=_gen(device, seed, wid, step, _F_ALPHA_A))
         out["alpha"].copy_(torch.exp(-torch.nn.functional.softplus(dt) * a))
     else:
-        g = torch.randn((B, T, H), dtype=torch.float64, device=device,
+        g = torch.randn(ashape, dtype=torch.float64, device=device,
                         generator=_gen(device, seed, wid, step, _F_ALPHA_DT))
         out["alpha"].copy_(torch.exp(-torch.nn.functional.softplus(g)))
     if shape.kind == "mamba2":

@@ -198,17 +198,113 @@ def test_p7_gdn_correction_rewrite():
                                    rtol=1e-12, atol=1e-13)
 
 
+# ----------------------------------------------------------------- KDA --
+
+def _run_tokens_kda(S0, alpha, beta, k, v, q):
+    S = S0.astype(np.float64).copy()
+    nh, T = beta.shape
+    out, u = oracle.kda_round(S, alpha, beta, k, v, q, np.full(nh, T, np.int32))
+    return out, u, S
+
+
+def _alpha_vec(nh, T, N, lo=0.3):
+    return RNG.uniform(lo, 1.0, (nh, T, N)).astype(np.float32)
+
+
+def test_kda_uniform_gate_is_gdn():
+    """A gate equal on every key channel reduces Kimi Delta Attention to Gated DeltaNet."""
+    d = _rand(unit_k=True)
+    nh, T, N = d["k"].shape
+    av = np.repeat(d["alpha"][:, :, None], N, axis=2)
+    o_kda, u_kda, S_kda = _run_tokens_kda(d["S0"], av, d["beta"], d["k"], d["v"], d["q"])
+    o_gdn, u_gdn, S_gdn = _run_tokens_gdn(d["S0"], d["alpha"], d["beta"], d["k"], d["v"], d["q"])
+    np.testing.assert_allclose(o_kda, o_gdn, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(u_kda, u_gdn, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S_kda, S_gdn, rtol=1e-12, atol=1e-12)
+
+
+def test_kda_beta_zero_decays_each_channel():
+    """beta = 0: S_t = S_0 Diag(prod of the gates up to t), so o_t = S_0 (Gamma_t * q_t), per channel."""
+    d = _rand()
+    nh, T, N = d["k"].shape
+    av = _alpha_vec(nh, T, N)
+    out, u, S = _run_tokens_kda(d["S0"], av, np.zeros_like(d["beta"]), d["k"], d["v"], d["q"])
+    G = np.cumprod(av.astype(np.float64), axis=1)  # [nh, T, N], includes token t's own gate
+    ref = np.einsum("hpn,htn->htp", d["S0"].astype(np.float64), G * d["q"].astype(np.float64))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(u == 0.0)
+
+
+def test_kda_beta_one_writes_value_at_key_when_gates_open():
+    """Gates all one, beta = 1, ||k_t|| = 1 exactly: S_t k_t = v_t, so q_t = k_t reads v_t."""
+    d = _rand()
+    nh, T, N = d["k"].shape
+    k = np.zeros((nh, T, N), np.float32)
+    for hd in range(nh):
+        for t in range(T):
+            idx = RNG.choice(N, 4, replace=False)
+            k[hd, t, idx] = RNG.choice([-0.5, 0.5], 4)
+    out, _, _ = _run_tokens_kda(d["S0"], np.ones((nh, T, N), np.float32), np.ones_like(d["beta"]), k, d["v"], k)
+    np.testing.assert_allclose(out, d["v"], rtol=1e-12, atol=1e-12)
+
+
+def test_kda_orthonormal_keys_column_recurrence():
+    """k_t = e_{t mod d}: column m follows a_m (1 - beta) S e_m + beta v when keyed, a_m S e_m otherwise."""
+    nh, T, P, N = 2, 11, 4, 4
+    d = _rand(nh=nh, T=T, P=P, N=N)
+    av = _alpha_vec(nh, T, N)
+    k = np.zeros((nh, T, N), np.float32)
+    for t in range(T):
+        k[:, t, t % N] = 1.0
+    out, u, S = _run_tokens_kda(d["S0"], av, d["beta"], k, d["v"], d["q"])
+    for hd in range(nh):
+        cols = [d["S0"][hd, :, m].astype(np.float64) for m in range(N)]
+        for t in range(T):
+            b = float(d["beta"][hd, t])
+            for m in range(N):
+                a = float(av[hd, t, m])
+                cols[m] = a * (1.0 - b) * cols[m] + b * d["v"][hd, t].astype(np.float64) if m == t % N else a * cols[m]
+            St = np.stack(cols, axis=1)
+            np.testing.assert_allclose(out[hd, t], St @ d["q"][hd, t].astype(np.float64), rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(S[hd], St, rtol=1e-11, atol=1e-11)
+
+
+def test_kda_projector_matrix_form_and_correction():
+    """S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T with explicit matrices, and
+    S_t = S_{t-1} Diag(a_t) + u_t k_t^T with u_t = beta_t (v_t - S_{t-1} (a_t * k_t))."""
+    d = _rand(T=6)
+    nh, T, N = d["k"].shape
+    av = _alpha_vec(nh, T, N)
+    out, u, _ = _run_tokens_kda(d["S0"], av, d["beta"], d["k"], d["v"], d["q"])
+    for hd in range(nh):
+        St = d["S0"][hd].astype(np.float64)
+        for t in range(T):
+            b = float(d["beta"][hd, t])
+            kt, vt = d["k"][hd, t].astype(np.float64), d["v"][hd, t].astype(np.float64)
+            Da = np.diag(av[hd, t].astype(np.float64))
+            ut = b * (vt - St @ (av[hd, t].astype(np.float64) * kt))
+            np.testing.assert_allclose(u[hd, t], ut, rtol=1e-11, atol=1e-12)
+            nxt = St @ Da @ (np.eye(N) - b * np.outer(kt, kt)) + b * np.outer(vt, kt)
+            np.testing.assert_allclose(nxt, St @ Da + np.outer(ut, kt), rtol=1e-11, atol=1e-12)
+            St = nxt
+            np.testing.assert_allclose(out[hd, t], St @ d["q"][hd, t], rtol=1e-11, atol=1e-11)
+
+
 # ------------------------------------------------ speculative semantics --
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_round_accepts_prefix_only(kind):
     """A round's draft outputs equal step-by-step decoding, and the state advances by acc only."""
-    d = _rand(nh=4, T=5, unit_k=(kind == "gdn"))
+    d = _rand(nh=4, T=5, unit_k=(kind != "mamba2"))
     nh, T = d["alpha"].shape
+    if kind == "kda":
+        d["alpha"] = _alpha_vec(nh, T, d["k"].shape[-1])
     acc = np.array([0, 2, 5, 1], np.int32)
     S = d["S0"].astype(np.float64).copy()
     if kind == "mamba2":
         out = oracle.mamba2_round(S, d["alpha"], d["k"], d["v"], d["q"], acc)
+    elif kind == "kda":
+        out, _ = oracle.kda_round(S, d["alpha"], d["beta"], d["k"], d["v"], d["q"], acc)
     else:
         out, _ = oracle.gdn_round(S, d["alpha"], d["beta"], d["k"], d["v"], d["q"], acc)
     for hd in range(nh):
@@ -217,6 +313,9 @@ def test_round_accepts_prefix_only(kind):
             sl = (slice(hd, hd + 1), slice(t, t + 1))
             if kind == "mamba2":
                 o = oracle.mamba2_round(Sx, d["alpha"][sl], d["k"][sl], d["v"][sl], d["q"][sl], np.ones(1, np.int32))
+            elif kind == "kda":
+                o, _ = oracle.kda_round(Sx, d["alpha"][sl], d["beta"][sl], d["k"][sl], d["v"][sl], d["q"][sl],
+                                        np.ones(1, np.int32))
             else:
                 o, _ = oracle.gdn_round(Sx, d["alpha"][sl], d["beta"][sl], d["k"][sl], d["v"][sl], d["q"][sl],
                                         np.ones(1, np.int32))
