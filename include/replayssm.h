@@ -63,7 +63,14 @@ extern "C" {
 /* ---- configuration ------------------------------------------------------ */
 enum replayssm_kind {
   REPLAYSSM_MAMBA2 = 0, /* S <- alpha S + v k^T                                  */
-  REPLAYSSM_GDN = 1     /* gated delta rule, stored as S <- alpha S + u k^T       */
+  REPLAYSSM_GDN = 1,    /* gated delta rule, stored as S <- alpha S + u k^T       */
+  REPLAYSSM_KDA = 2     /* Kimi Delta Attention: the delta rule with a gate per key
+                           channel, S <- S Diag(a) (I - beta k k^T) + beta v k^T,
+                           stored as S <- S Diag(a) + u k^T with
+                           u = beta (v - S (a * k)). Named compatible but not built
+                           on the summary page (Limits); FP32 precision only.
+                           Every alpha input below, [...][H] for the other kinds,
+                           is [...][H][dk] for KDA (a gate row per record)         */
 };
 
 enum replayssm_precision {
@@ -94,8 +101,8 @@ typedef struct replayssm_config {
  *                                    (NULL in BF16_SHARED mode)
  *  lp          uint16 [B][H][dv*dk]  bf16 checkpoint bits, library-defined
  *                                    layout (NULL in FP32 mode)
- *  ring_alpha  float  [B][H][C]
- *  ring_beta   float  [B][H][C]      GDN only, else NULL
+ *  ring_alpha  float  [B][H][C]      (KDA: [B][H][C][dk], one gate per key channel)
+ *  ring_beta   float  [B][H][C]      GDN and KDA, else NULL
  *  ring_k      float  [B][H][C][dk]
  *  ring_v      float  [B][H][C][dv]  Mamba-2: v. GDN: v as appended, replaced by
  *                                    the correction u_t = beta_t (v_t - alpha_t
@@ -180,7 +187,8 @@ int replayssm_read_error(const replayssm_state* st, int32_t* err_out, void* stre
  * to ring slot (head + h + p + i) mod C, then p += T ("How it works":
  * Standard decoding appends the token's (alpha, v, k); Speculative decoding
  * appends all T draft records; the buffer is circular with capacity L + T).
- *   alpha [B][T][H], k [B][T][H][dk], v [B][T][H][dv], beta [B][T][H] (GDN, else NULL)
+ *   alpha [B][T][H] (KDA: [B][T][H][dk]), k [B][T][H][dk], v [B][T][H][dv],
+ *   beta [B][T][H] (GDN and KDA, else NULL)
  * 1 <= T <= T_max. A sequence with p + T > T_max is skipped and flagged
  * (REPLAYSSM_DEVERR_APPEND_OVERFLOW). */
 int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int T,

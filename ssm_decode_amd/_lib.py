@@ -21,10 +21,10 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libreplayssm.so")
 
-MAMBA2, GDN = 0, 1
+MAMBA2, GDN, KDA = 0, 1, 2
 FP32, FP32_HP_BF16_LP, BF16_SHARED = 0, 1, 2
 PRECISIONS = {"fp32": FP32, "fp32_hp_bf16_lp": FP32_HP_BF16_LP, "bf16_shared": BF16_SHARED}
-KINDS = {"mamba2": MAMBA2, "gdn": GDN}
+KINDS = {"mamba2": MAMBA2, "gdn": GDN, "kda": KDA}
 
 OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
 DEVERR_APPEND_OVERFLOW, DEVERR_PENDING, DEVERR_ACCEPT, DEVERR_CORRUPT, DEVERR_STALE, DEVERR_INDEX = 1, 2, 4, 8, 16, 32
@@ -258,7 +258,8 @@ class LayerState:
         f32, i32 = torch.float32, torch.int32
         self.hp = torch.zeros((B, H, dv * dk), dtype=f32, device=device) if sz.hp_bytes else None
         self.lp = torch.zeros((B, H, dv * dk), dtype=torch.int16, device=device) if sz.lp_bytes else None
-        self.ring_alpha = torch.zeros((B, H, C), dtype=f32, device=device)
+        # a scalar gate per record, or (KDA) a gate row of dk channels
+        self.ring_alpha = torch.zeros((B, H, C, dk) if cfg.kind == KDA else (B, H, C), dtype=f32, device=device)
         self.ring_beta = torch.zeros((B, H, C), dtype=f32, device=device) if sz.ring_beta_bytes else None
         self.ring_k = torch.zeros((B, H, C, dk), dtype=f32, device=device)
         self.ring_v = torch.zeros((B, H, C, dv), dtype=f32, device=device)

@@ -54,7 +54,7 @@ bool exact_u(const replayssm_config* c) {
 
 int check_config(const replayssm_config* c) {
   if (c == nullptr) return fail(REPLAYSSM_EINVAL, "cfg is NULL");
-  if (c->kind != REPLAYSSM_MAMBA2 && c->kind != REPLAYSSM_GDN)
+  if (c->kind != REPLAYSSM_MAMBA2 && c->kind != REPLAYSSM_GDN && c->kind != REPLAYSSM_KDA)
     return fail(REPLAYSSM_EINVAL, "kind %d unknown", c->kind);
   if (c->precision < REPLAYSSM_FP32 || c->precision > REPLAYSSM_BF16_SHARED)
     return fail(REPLAYSSM_EINVAL, "precision %d unknown", c->precision);
@@ -70,11 +70,14 @@ int check_config(const replayssm_config* c) {
     return fail(REPLAYSSM_EINVAL, "T_max=%d outside 1..min(8, L)", c->T_max);
   if (c->precision != REPLAYSSM_FP32 && c->dk % 32 != 0)
     return fail(REPLAYSSM_ENOTSUP, "a bf16 checkpoint needs dk %% 32 == 0 (dk=%d)", c->dk);
+  if (c->kind == REPLAYSSM_KDA && c->precision != REPLAYSSM_FP32)
+    return fail(REPLAYSSM_ENOTSUP, "KDA layers keep an fp32 checkpoint only (precision FP32)");
   if (c->precision == REPLAYSSM_BF16_SHARED && c->kind == REPLAYSSM_GDN)
     return fail(REPLAYSSM_ENOTSUP,
                 "the shared bf16 checkpoint is built for Mamba-2 only (GDN takes FP32 or "
                 "FP32_HP_BF16_LP)");
-  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max), exact_u(c));
+  const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max),
+                          exact_u(c) ? rs::kKindGdnExact : c->kind);
   if (lds.total * 4 > rs::kMaxLdsBytes)
     return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
                 rs::kMaxLdsBytes);
@@ -88,7 +91,7 @@ int check_state(const replayssm_config* c, const replayssm_state* s) {
   NEED(s->ring_alpha);
   NEED(s->ring_k);
   NEED(s->ring_v);
-  if (c->kind == REPLAYSSM_GDN) NEED(s->ring_beta);
+  if (c->kind != REPLAYSSM_MAMBA2) NEED(s->ring_beta);
   if (exact_u(c)) NEED(s->ring_vraw);
   NEED(s->head);
   NEED(s->h);
@@ -161,8 +164,8 @@ int replayssm_get_sizes(const replayssm_config* cfg, replayssm_sizes* out) {
   out->alignment = 256;
   out->hp_bytes = cfg->precision == REPLAYSSM_BF16_SHARED ? 0 : state * 4;
   out->lp_bytes = cfg->precision == REPLAYSSM_FP32 ? 0 : state * 2;
-  out->ring_alpha_bytes = BH * C * 4;
-  out->ring_beta_bytes = cfg->kind == REPLAYSSM_GDN ? BH * C * 4 : 0;
+  out->ring_alpha_bytes = BH * C * 4 * (cfg->kind == REPLAYSSM_KDA ? cfg->dk : 1);
+  out->ring_beta_bytes = cfg->kind != REPLAYSSM_MAMBA2 ? BH * C * 4 : 0;
   out->ring_k_bytes = BH * C * cfg->dk * 4;
   out->ring_v_bytes = BH * C * cfg->dv * 4;
   out->ptr_bytes = (int64_t)cfg->B * 4;
@@ -229,7 +232,7 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
   NEED(alpha);
   NEED(k);
   NEED(v);
-  if (cfg->kind == REPLAYSSM_GDN) NEED(beta);
+  if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
   rs::AppendArgs a{};
   a.ring_alpha = st->ring_alpha;
   a.ring_beta = st->ring_beta;
@@ -242,7 +245,7 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
   a.arrive = st->arrive;
   a.err = st->err;
   a.alpha = alpha;
-  a.beta = cfg->kind == REPLAYSSM_GDN ? beta : nullptr;
+  a.beta = cfg->kind != REPLAYSSM_MAMBA2 ? beta : nullptr;
   a.k = k;
   a.v = v;
   a.B = cfg->B;
@@ -252,7 +255,8 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
   a.C = cfg->L + cfg->T_max;
   a.T = T;
   a.T_max = cfg->T_max;
-  a.units_per_seq = T * cfg->H * (cfg->dk + cfg->dv) / 4;
+  // float4 units per sequence: k rows, KDA gate rows, v rows
+  a.units_per_seq = T * cfg->H * ((cfg->kind == REPLAYSSM_KDA ? 2 : 1) * cfg->dk + cfg->dv) / 4;
   return hip_result(rs::launch_append(cfg->kind, a, as_stream(stream)), "append");
 }
 
@@ -289,10 +293,10 @@ static int fused_call(const replayssm_config* cfg, const replayssm_state* st, in
   NEED(v);
   NEED(q);
   NEED(out);
-  if (cfg->kind == REPLAYSSM_GDN) NEED(beta);
+  if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
   rs::ReplayArgs a = replay_args(cfg, st, T, mode, q, out);
   a.in_alpha = alpha;
-  a.in_beta = cfg->kind == REPLAYSSM_GDN ? beta : nullptr;
+  a.in_beta = cfg->kind != REPLAYSSM_MAMBA2 ? beta : nullptr;
   a.in_k = k;
   a.in_v = v;
   a.fused = 1;
@@ -379,7 +383,7 @@ int replayssm_eager_step(const replayssm_config* cfg, float* S, const float* alp
   NEED(v);
   NEED(q);
   NEED(out);
-  if (cfg->kind == REPLAYSSM_GDN) NEED(beta);
+  if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
   rs::EagerArgs a{};
   a.S = S;
   a.slot = nullptr;
@@ -411,7 +415,7 @@ int replayssm_eager_verify(const replayssm_config* cfg, float* pool, const int32
   NEED(v);
   NEED(q);
   NEED(out);
-  if (cfg->kind == REPLAYSSM_GDN) NEED(beta);
+  if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
   rs::EagerArgs a{};
   a.S = pool;
   a.slot = slot;

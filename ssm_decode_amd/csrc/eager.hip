@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(1024) eager_kernel(const EagerArgs a) {
 
   for (int i = 0; i < T; ++i) {
     const int64_t tok = ((int64_t)b * T + i) * H + hd;
-    const float al = a.alpha[tok];
+    const float al = KIND == REPLAYSSM_KDA ? 1.f : a.alpha[tok];
     const float* kin = a.k + tok * DK + 4 * g;
     const float* qin = a.q + tok * DK + 4 * g;
     f32x4 kf[NT];
@@ -50,6 +50,17 @@ __global__ void __launch_bounds__(1024) eager_kernel(const EagerArgs a) {
       for (int nt = 0; nt < NT; ++nt) w += dot4(S[nt], kf[nt]);
       w = sum_groups(w);
       coef = a.beta[tok] * (vp - al * w);  // u = beta (v - alpha S k)
+    }
+    if constexpr (KIND == REPLAYSSM_KDA) {
+      // per-channel gate: w = S (a * k), u = beta (v - w), S <- S Diag(a) + u k^T
+      const float* ain = a.alpha + tok * DK + 4 * g;
+      float w = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) w += dot4(S[nt], ld4(ain + nt * 16) * kf[nt]);
+      w = sum_groups(w);
+      coef = a.beta[tok] * (vp - w);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S[nt] *= ld4(ain + nt * 16);
     }
     float o = 0.f;
 #pragma unroll
@@ -81,6 +92,7 @@ static hipError_t launch_kind(int dk, const EagerArgs& a, hipStream_t s) {
 
 hipError_t launch_eager(int kind, int dk, const EagerArgs& a, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
+  if (kind == REPLAYSSM_KDA) return launch_kind<REPLAYSSM_KDA>(dk, a, s);
   return kind == REPLAYSSM_GDN ? launch_kind<REPLAYSSM_GDN>(dk, a, s)
                                : launch_kind<REPLAYSSM_MAMBA2>(dk, a, s);
 }

@@ -38,7 +38,8 @@ enum Mode : int { kModeDecode = 0, kModeVerify = 1, kModeFlush = 2 };
 // Kernel kinds: the two public kinds, plus GDN with the two-precision checkpoint,
 // whose folds recompute the folded records' corrections (its own instantiation,
 // so that the other GDN kernels do not carry that code's registers).
-constexpr int kKindGdnExact = 2;
+constexpr int kKindGdnExact = 3;
+// Kinds whose records carry a correction u and a beta (the delta rule).
 __host__ __device__ constexpr bool kind_gdn(int kind) { return kind != REPLAYSSM_MAMBA2; }
 
 struct ReplayArgs {
@@ -105,32 +106,39 @@ struct EagerArgs {
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
 // wavefront reading one column of four consecutive rows hit distinct banks;
 // windows too long for that within kMaxLdsBytes use unpadded rows instead.
-// With gram (GDN with the two-precision checkpoint) one more block holds the
-// Gram matrix k_i . k_j of the staged records for the exact fold.
+// The kernel kind changes blocks: GDN with the two-precision checkpoint adds the
+// Gram matrix k_i . k_j of the staged records (its exact fold); KDA has a gate
+// row per record instead of a scalar, no decay-product tables, and adds the
+// drafts' queries and keys scaled by the gates since the last committed record,
+// and the committed records' column decay.
 constexpr int kMaxLdsBytes = 64 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, gram, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, gram, qg, kg, pf, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
-  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, bool with_gram = false) {
-    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), with_gram);
-    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, with_gram);
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, int kind = REPLAYSSM_MAMBA2) {
+    carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), kind);
+    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, kind);
   }
-  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, bool with_gram) {
+  __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, int kind) {
+    const bool with_gram = kind == kKindGdnExact, kda = kind == REPLAYSSM_KDA;
     dks = kstride;
     dvs = vstride;
     k = 0;
     v = k + C * dks;
     alpha = v + C * dvs;
-    beta = alpha + pad4(C);
+    beta = alpha + (kda ? C * dks : pad4(C));
     q = beta + pad4(C);
     gq = q + tmax * dk;
-    gk = gq + pad4((C + 1) * tmax);
-    cq = gk + pad4((C + 1) * tmax);
+    gk = gq + (kda ? 0 : pad4((C + 1) * tmax));
+    cq = gk + (kda ? 0 : pad4((C + 1) * tmax));
     ck = cq + pad4(C * tmax);
     gram = ck + pad4(C * tmax);
-    total = gram + (with_gram ? pad4(C * C) : 0);
+    qg = gram + (with_gram ? pad4(C * C) : 0);
+    kg = qg + (kda ? tmax * dk : 0);
+    pf = kg + (kda ? tmax * dk : 0);
+    total = pf + (kda ? dk : 0);
   }
 };
 

@@ -1,5 +1,6 @@
 // Replay kernel of libreplayssm: standard decode, output-only draft
-// verification and the checkpoint fold, for Mamba-2 and Gated DeltaNet heads.
+// verification and the checkpoint fold, for Mamba-2, Gated DeltaNet and Kimi
+// Delta Attention (per-channel gate) heads.
 //
 // The work items are (sequence b, head) pairs. A workgroup holds one item at a
 // time, one wavefront per 16-row tile of the head's state (dv / 16
@@ -27,7 +28,9 @@
 //     exact);
 //  5. GDN: u_i = beta_i (v_i - alpha_i S_{i-1} k_i) with S_{i-1} k_i rebuilt
 //     from S k_i and the buffer ("How it works": Gated DeltaNet), sequential
-//     over the drafts, and stored in place of v_i;
+//     over the drafts, and stored in place of v_i; KDA: the same with a gate
+//     vector per record, whose products are applied to the staged keys and
+//     queries per channel instead of being tabulated per record;
 //  6. the pointers are only read while items run; the last workgroup of the
 //     grid to finish advances them for every sequence.
 //
@@ -94,6 +97,7 @@ template <int TMAX>
 struct RecRegs {
   static constexpr int K = 2, V = 1;
   f32x4 kb[K], vb[V], qv;
+  f32x4 ab[K];  // KDA: the gate rows, staged like the k rows (unused by the other kinds)
   float al, be;
 };
 
@@ -158,6 +162,11 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
     const float* src = (fused && r >= p.h) ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck
                                            : s.rk + ring_slot(p.head, r, C) * DK + 4 * m.ck;
     rr.kb[j] = ld4(r < R ? src : a.ring_k);
+    if constexpr (KIND == REPLAYSSM_KDA) {
+      const float* asrc = (fused && r >= p.h) ? a.in_alpha + (s.ia + (int64_t)(r - p.h) * H) * DK + 4 * m.ck
+                                              : a.ring_alpha + (s.bhC + ring_slot(p.head, r, C)) * DK + 4 * m.ck;
+      rr.ab[j] = ld4(r < R ? asrc : a.ring_alpha);
+    }
   }
   // a fold with exact corrections stages the committed records' raw v instead of
   // their stored corrections
@@ -171,7 +180,7 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
   }
   // q is read once per call: non-temporal, like the checkpoint stream
   rr.qv = ld4_stream(m.rk0 < T ? a.q + (((int64_t)b * T + m.rk0) * H + hd) * DK + 4 * m.ck : a.ring_k);
-  {
+  if constexpr (KIND != REPLAYSSM_KDA) {
     const float* src = (fused && tid >= p.h) ? a.in_alpha + s.ia + (int64_t)(tid - p.h) * H
                                              : a.ring_alpha + s.bhC + ring_slot(p.head, tid, C);
     rr.al = *(tid < R ? src : a.ring_alpha);
@@ -207,6 +216,12 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     const f32x4 x = ld4(in ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck : s.rk + slot * DK + 4 * m.ck);
     st4(sm + lds.k + r * lds.dks + 4 * m.ck, x);
     if (in) st4(wk + slot * DK + 4 * m.ck, x);
+    if constexpr (KIND == REPLAYSSM_KDA) {
+      float* ra = a.ring_alpha + (s.bhC + slot) * DK + 4 * m.ck;
+      const f32x4 y = ld4(in ? a.in_alpha + (s.ia + (int64_t)(r - p.h) * H) * DK + 4 * m.ck : ra);
+      st4(sm + lds.alpha + r * lds.dks + 4 * m.ck, y);
+      if (in) st4(ra, y);
+    }
   }
   for (int r = m.rv0 + kRecV * 16; r < R; r += 16) {
     const int slot = ring_slot(p.head, r, C);
@@ -222,9 +237,11 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   for (int r = tid + nthr; r < R; r += nthr) {
     const int slot = ring_slot(p.head, r, C);
     const bool in = fused && r >= p.h;
-    const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
-    sm[lds.alpha + r] = al;
-    if (in) a.ring_alpha[s.bhC + slot] = al;
+    if constexpr (KIND != REPLAYSSM_KDA) {
+      const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
+      sm[lds.alpha + r] = al;
+      if (in) a.ring_alpha[s.bhC + slot] = al;
+    }
     if (GDN && (r >= p.h || raw)) {
       const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
       sm[lds.beta + r] = be;
@@ -237,6 +254,10 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     if (r < R) {
       st4(sm + lds.k + r * lds.dks + 4 * m.ck, rr.kb[j]);
       if (fused && r >= p.h) st4(wk + ring_slot(p.head, r, C) * DK + 4 * m.ck, rr.kb[j]);
+      if constexpr (KIND == REPLAYSSM_KDA) {
+        st4(sm + lds.alpha + r * lds.dks + 4 * m.ck, rr.ab[j]);
+        if (fused && r >= p.h) st4(a.ring_alpha + (s.bhC + ring_slot(p.head, r, C)) * DK + 4 * m.ck, rr.ab[j]);
+      }
     }
   }
 #pragma unroll
@@ -253,8 +274,10 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   for (int i = (m.rk0 < T ? m.rk0 + m.kstep : m.rk0); i < TMAX; i += m.kstep)
     if (i >= T) st4(sm + lds.q + i * DK + 4 * m.ck, f32x4{0.f, 0.f, 0.f, 0.f});  // rows of absent drafts
   if (tid < R) {
-    sm[lds.alpha + tid] = rr.al;
-    if (fused && tid >= p.h) a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)] = rr.al;
+    if constexpr (KIND != REPLAYSSM_KDA) {
+      sm[lds.alpha + tid] = rr.al;
+      if (fused && tid >= p.h) a.ring_alpha[s.bhC + ring_slot(p.head, tid, C)] = rr.al;
+    }
     if (GDN && (tid >= p.h || raw)) {
       sm[lds.beta + tid] = rr.be;
       if (fused && tid >= p.h) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
@@ -274,6 +297,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
   constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
   constexpr bool GDN = kind_gdn(KIND);
+  constexpr bool KDA = KIND == REPLAYSSM_KDA;
 
   // The thread index is laundered per item: without it the compiler hoists
   // every thread-derived address out of the item loop and keeps them all live
@@ -291,7 +315,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int hd = item - b * H;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
-  const ReplayLds lds(C, DK, dv, TMAX, KIND == kKindGdnExact);
+  const ReplayLds lds(C, DK, dv, TMAX, KIND);
   const StageMap map(tid, nthr, LPR, dv);
 
   const int mode = a.mode;
@@ -313,6 +337,42 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // ---- the next item's ring rows: requested now, waited for by the next item
   const bool more = next < a.B * a.H;
   load_records<KIND, NT, TMAX, FUSED>(a, next, nptr, nrt, more, tid, map, rr);
+
+  // ---- KDA: the gate products, per channel (a thread per channel and job) ------
+  // With per-channel gates the state after records [0, m] is
+  //   S_m = S Diag(prod of a_r, r <= m) + sum_r u_r (k_r * prod of a_s, r < s <= m)^T,
+  // so the products go onto the vectors instead of into decay tables:
+  //  - committed records: k_j <- k_j * prod of a over (j, hc) in place, and
+  //    pf = prod of a over [0, hc), so that S_h = S Diag(pf) + sum_j u_j k_j^T;
+  //  - drafts: Gamma_i = prod of a over [hc, hc + i], qg_i = Gamma_i * q_i and
+  //    kg_i = Gamma_i * k_{hc+i}: o_i needs S_h qg_i and u_i needs S_h kg_i
+  //    (the draft's own gate sits in kg_i, as S_{m-1} (a_m * k_m) requires);
+  //  - draft-to-draft terms take the gates between the two drafts, applied
+  //    in the dot-product pass.
+  if constexpr (KDA) {
+    if (work) {
+      for (int u = tid; u < 2 * DK; u += nthr) {
+        if (u < DK) {
+          const int n = u;
+          float s = 1.f;
+          for (int j = hc - 1; j >= 0; --j) {
+            sm[lds.k + j * lds.dks + n] *= s;
+            s *= sm[lds.alpha + j * lds.dks + n];
+          }
+          sm[lds.pf + n] = s;
+        } else {
+          const int n = u - DK;
+          float gm = 1.f;
+          for (int i = 0; i < T; ++i) {
+            gm *= sm[lds.alpha + (hc + i) * lds.dks + n];
+            sm[lds.qg + i * DK + n] = gm * sm[lds.q + i * DK + n];
+            sm[lds.kg + i * DK + n] = gm * sm[lds.k + (hc + i) * lds.dks + n];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
   // the next item's checkpoint copy, requested once S is free (same loads on every path). The
   // empty asm marks every S register as read here, on every path: no load into S can still be
   // pending when S is reloaded, so the compiler's waits before the reload stay at zero.
@@ -338,8 +398,10 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
         if (i < T) {
-          yq[i] += dot4(S[nt], ld4(sm + lds.q + i * DK + nt * 16 + 4 * g));
-          if (GDN) yk[i] += dot4(S[nt], ld4(sm + lds.k + (hc + i) * lds.dks + nt * 16 + 4 * g));
+          const float* qi = KDA ? sm + lds.qg + i * DK : sm + lds.q + i * DK;
+          const float* ki = KDA ? sm + lds.kg + i * DK : sm + lds.k + (hc + i) * lds.dks;
+          yq[i] += dot4(S[nt], ld4(qi + nt * 16 + 4 * g));
+          if (GDN) yk[i] += dot4(S[nt], ld4(ki + nt * 16 + 4 * g));
         }
       }
     }
@@ -353,7 +415,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // Each product set is one suffix-product scan across a wavefront (lane l
   // stands for record first + l), one wavefront per end point.
   auto scans_and_dots = [&]() {
-  if (outputs) {
+  if (!KDA && outputs) {
     const bool wide = R - r0 + 1 > kWave;
     if (!wide) {
       for (int job = wave; job < 2 * T; job += W) {
@@ -399,13 +461,28 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       const bool valid = r < R;
       f32x4 kr = f32x4{0.f, 0.f, 0.f, 0.f};
       if (valid) kr = ld4(sm + lds.k + r * lds.dks + 4 * li);
+      f32x4 dec = {1.f, 1.f, 1.f, 1.f};  // KDA: gates of records (r, hc + i] for a draft row r
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
         if (i < T) {
-          const float dq = sum_width<LPR>(dot4(kr, ld4(sm + lds.q + i * DK + 4 * li)));
+          f32x4 kx = kr;
+          const float* qrow = sm + lds.q + i * DK + 4 * li;
+          const float* krow = sm + lds.k + (hc + i) * lds.dks + 4 * li;
+          if constexpr (KDA) {
+            if (r < hc) {
+              // a committed row (already carried to the last committed record)
+              // meets the drafts' gated vectors
+              qrow = sm + lds.qg + i * DK + 4 * li;
+              krow = sm + lds.kg + i * DK + 4 * li;
+            } else {
+              if (i > r - hc) dec *= ld4(sm + lds.alpha + (hc + i) * lds.dks + 4 * li);
+              kx = kr * dec;
+            }
+          }
+          const float dq = sum_width<LPR>(dot4(kx, ld4(qrow)));
           if (valid && li == 0) sm[lds.cq + r * TMAX + i] = dq;
           if constexpr (GDN) {
-            const float dkk = sum_width<LPR>(dot4(kr, ld4(sm + lds.k + (hc + i) * lds.dks + 4 * li)));
+            const float dkk = sum_width<LPR>(dot4(kx, ld4(krow)));
             if (valid && li == 0) sm[lds.ck + r * TMAX + i] = dkk;
           }
         }
@@ -505,22 +582,26 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       }
       return;
     }
-    float gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
+    // (KDA: the column decay is already applied and the keys carry the rest)
+    float gf = 1.f;
+    if constexpr (!KDA) {
+      gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const float y = __shfl_down(gf, d, kWave);
-      if (lane + d < kWave) gf *= y;
+      for (int d = 1; d < kWave; d <<= 1) {
+        const float y = __shfl_down(gf, d, kWave);
+        if (lane + d < kWave) gf *= y;
+      }
+      const float G = __shfl(gf, 0, kWave);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S[nt] *= G;
     }
-    const float G = __shfl(gf, 0, kWave);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) S[nt] *= G;
     // MFMA 16x16x4: A[m][kk] = k_j[16 nt + m], B[kk][n] = gamma_j v_j[16 wave + n],
     // j = 4 kc + kk; lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15].
     const int nkc = (hc + 3) >> 2;
     for (int kc = 0; kc < nkc; ++kc) {
       const int j = 4 * kc + g;
       const bool vj = j < hc;
-      const float wj = __shfl(gf, (j + 1) & (kWave - 1), kWave);  // gf_{j+1}; j + 1 = 64 only if hc = 64
+      const float wj = KDA ? 1.f : __shfl(gf, (j + 1) & (kWave - 1), kWave);  // gf_{j+1}; j + 1 = 64 only if hc = 64
       const float bval = vj ? (j + 1 < kWave ? wj : 1.f) * sm[lds.v + j * lds.dvs + prow] : 0.f;
       const float* krow = sm + lds.k + (vj ? j : 0) * lds.dks + col;
 #pragma unroll
@@ -543,6 +624,10 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     const float* cq = sm + lds.cq;
     const float* ck = sm + lds.ck;
     const float* sv = sm + lds.v + prow;
+    // decay factors of the output and correction sums (KDA: the gates are on the
+    // staged vectors and every factor is 1)
+    auto fq = [&](int idx) { return KDA ? 1.f : gq[idx]; };
+    auto fk = [&](int idx) { return KDA ? 1.f : gk[idx]; };
     if constexpr (!GDN) {
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
@@ -562,12 +647,12 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         wc[i] = 0.f;
         oc[i] = 0.f;
         if (i < T) {
-          wc[i] = gk[r0 * TMAX + i] * yk[i];
-          oc[i] = gq[r0 * TMAX + i] * yq[i];
+          wc[i] = fk(r0 * TMAX + i) * yk[i];
+          oc[i] = fq(r0 * TMAX + i) * yq[i];
           for (int r = r0 + g; r < hc; r += 4) {
             const float u = sv[r * lds.dvs];
-            wc[i] += gk[(r + 1) * TMAX + i] * ck[r * TMAX + i] * u;
-            oc[i] += gq[(r + 1) * TMAX + i] * cq[r * TMAX + i] * u;
+            wc[i] += fk((r + 1) * TMAX + i) * ck[r * TMAX + i] * u;
+            oc[i] += fq((r + 1) * TMAX + i) * cq[r * TMAX + i] * u;
           }
           wc[i] = sum_groups(wc[i]);
           oc[i] = sum_groups(oc[i]);
@@ -581,13 +666,13 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         if (i < T) {
           float w = wc[i];
 #pragma unroll
-          for (int d = 0; d < i; ++d) w += gk[(hc + d + 1) * TMAX + i] * ck[(hc + d) * TMAX + i] * ud[d];
-          const float al = sm[lds.alpha + hc + i];
+          for (int d = 0; d < i; ++d) w += fk((hc + d + 1) * TMAX + i) * ck[(hc + d) * TMAX + i] * ud[d];
+          const float al = KDA ? 1.f : sm[lds.alpha + hc + i];
           const float be = sm[lds.beta + hc + i];
           ud[i] = be * (sv[(hc + i) * lds.dvs] - al * w);
           float o = oc[i];
 #pragma unroll
-          for (int d = 0; d <= i; ++d) o += gq[(hc + d + 1) * TMAX + i] * cq[(hc + d) * TMAX + i] * ud[d];
+          for (int d = 0; d <= i; ++d) o += fq((hc + d + 1) * TMAX + i) * cq[(hc + d) * TMAX + i] * ud[d];
           if (g == 0) {
             __builtin_nontemporal_store(o, a.out + (((int64_t)b * T + i) * H + hd) * dv + prow);
             int slot = head + hc + i;
@@ -606,6 +691,13 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // control-flow path, and a path without the request would make them drain.
   if constexpr (NT >= 2) {
     if (lp) widen_lp<NT>(S);  // (the shared-bf16 mode also folds from the bf16 values)
+  }
+  if constexpr (KDA) {
+    // S Diag(pf): the checkpoint carried over the committed records' gates
+    if (work && hc > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S[nt] *= ld4(sm + lds.pf + nt * 16 + 4 * g);
+    }
   }
   if (fold) fold_state();
   if (outputs) matvec();
@@ -721,7 +813,7 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
 
 template <int KIND, int NT, int TMAX, bool FUSED>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND == kKindGdnExact);
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
   const int block = a.dv / 16 * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
@@ -763,6 +855,7 @@ hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStr
   if (a.B * a.H == 0) return hipSuccess;
   if (kind == REPLAYSSM_GDN && a.precision == REPLAYSSM_FP32_HP_BF16_LP)
     return launch_kind<kKindGdnExact>(dk, tmax, a, s);
+  if (kind == REPLAYSSM_KDA) return launch_kind<REPLAYSSM_KDA>(dk, tmax, a, s);
   return kind == REPLAYSSM_GDN ? launch_kind<REPLAYSSM_GDN>(dk, tmax, a, s)
                                : launch_kind<REPLAYSSM_MAMBA2>(dk, tmax, a, s);
 }

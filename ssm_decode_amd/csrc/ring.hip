@@ -64,21 +64,30 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
     const int nk = T * H * dk4;
     const float* ksrc = a.k + (int64_t)b * T * H * dk;
     const float* vsrc = a.v + (int64_t)b * T * H * dv;
+    // units: the k rows, then (KDA) the gate rows, then the v rows
+    const int nka = KIND == REPLAYSSM_KDA ? 2 * nk : nk;
+    const float* asrc = a.alpha + (int64_t)b * T * H * dk;
     for (int u = blockIdx.x * 256 + threadIdx.x; u < a.units_per_seq; u += gridDim.x * 256) {
-      if (u < nk) {
-        const int c4 = u % dk4, th = u / dk4;
+      if (u < nka) {
+        const bool gate = u >= nk;
+        const int uk = gate ? u - nk : u;
+        const int c4 = uk % dk4, th = uk / dk4;
         const int hd = th % H, i = th / H;
         const int slot = (first + i) % C;
-        st4(a.ring_k + (((int64_t)b * H + hd) * C + slot) * dk + 4 * c4, ld4(ksrc + 4 * (int64_t)u));
+        const int64_t dst = (((int64_t)b * H + hd) * C + slot) * dk + 4 * c4;
+        if (gate)
+          st4(a.ring_alpha + dst, ld4(asrc + 4 * (int64_t)uk));
+        else
+          st4(a.ring_k + dst, ld4(ksrc + 4 * (int64_t)uk));
       } else {
-        const int uv = u - nk;
+        const int uv = u - nka;
         const int c4 = uv % dv4, th = uv / dv4;
         const int hd = th % H, i = th / H;
         const int slot = (first + i) % C;
         const int64_t dst = (((int64_t)b * H + hd) * C + slot) * dv + 4 * c4;
         const f32x4 x = ld4(vsrc + 4 * (int64_t)uv);
         st4(a.ring_v + dst, x);
-        if (KIND == REPLAYSSM_GDN && a.ring_vraw) st4(a.ring_vraw + dst, x);
+        if (KIND != REPLAYSSM_MAMBA2 && a.ring_vraw) st4(a.ring_vraw + dst, x);
       }
     }
     if (blockIdx.x == 0) {
@@ -87,8 +96,8 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
         const int slot = (first + i) % C;
         const int64_t dst = ((int64_t)b * H + hd) * C + slot;
         const int64_t src = ((int64_t)b * T + i) * H + hd;
-        a.ring_alpha[dst] = a.alpha[src];
-        if (KIND == REPLAYSSM_GDN) a.ring_beta[dst] = a.beta[src];
+        if (KIND != REPLAYSSM_KDA) a.ring_alpha[dst] = a.alpha[src];
+        if (KIND != REPLAYSSM_MAMBA2) a.ring_beta[dst] = a.beta[src];
       }
     }
   }
@@ -106,7 +115,9 @@ hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s) {
   int chunks = (a.units_per_seq + per_block - 1) / per_block;
   if (chunks < 1) chunks = 1;
   const dim3 grid((unsigned)chunks, (unsigned)a.B);
-  if (kind == REPLAYSSM_GDN)
+  if (kind == REPLAYSSM_KDA)
+    hipLaunchKernelGGL(append_kernel<REPLAYSSM_KDA>, grid, dim3(256), 0, s, a);
+  else if (kind == REPLAYSSM_GDN)
     hipLaunchKernelGGL(append_kernel<REPLAYSSM_GDN>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(append_kernel<REPLAYSSM_MAMBA2>, grid, dim3(256), 0, s, a);

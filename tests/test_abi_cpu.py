@@ -65,6 +65,9 @@ def test_sizes_of_the_b256_mamba2_layer(rs):
     s5 = rs.get_sizes(rs.make_config("gdn", "fp32_hp_bf16_lp", 256, 32, 128, 128, 16, 4))
     assert s5.ring_vraw_bytes == s5.ring_v_bytes == 256 * 32 * 20 * 128 * 4 and s5.lp_bytes == s5.hp_bytes // 2
     assert s2.ring_vraw_bytes == 0
+    s6 = rs.get_sizes(rs.make_config("kda", "fp32", 256, 32, 128, 128, 16, 4))
+    assert s6.ring_alpha_bytes == 256 * 32 * 20 * 128 * 4 and s6.ring_beta_bytes == 256 * 32 * 20 * 4
+    assert s6.ring_vraw_bytes == 0 and s6.hp_bytes == 256 * 32 * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("L,T", [(4, 1), (4, 4), (8, 8), (16, 8), (32, 8), (64, 1), (64, 4)])
@@ -82,6 +85,8 @@ def test_window_sweep_configs_fit(rs, L, T):
     (dict(precision="fp32_hp_bf16_lp", dk=16, dv=16), -2), (dict(kind="gdn", precision="bf16_shared"), -2),
     (dict(kind="gdn", precision="fp32_hp_bf16_lp", L=64, T_max=4, dv=128), -2),
     (dict(L=64, T_max=8, dv=256, dk=128), -2), (dict(L=64, T_max=8), -2),
+    (dict(kind="kda", precision="fp32_hp_bf16_lp"), -2), (dict(kind="kda", precision="bf16_shared"), -2),
+    (dict(kind="kda", L=64, T_max=8, dv=128), -2), (dict(kind="kda"), 0), (dict(kind="kda", dk=16, dv=16, L=64), 0),
 ])
 def test_config_validation(rs, kw, code):
     base = dict(kind="mamba2", precision="fp32", B=2, H=3, dv=64, dk=128, L=16, T_max=4)

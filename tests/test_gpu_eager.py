@@ -28,7 +28,8 @@ def _packed(cfg, S0, nslots=1):
     return pool
 
 
-@pytest.mark.parametrize("kind,P,N", [("mamba2", 64, 128), ("gdn", 128, 128), ("mamba2", 16, 16), ("gdn", 32, 64)])
+@pytest.mark.parametrize("kind,P,N", [("mamba2", 64, 128), ("gdn", 128, 128), ("mamba2", 16, 16), ("gdn", 32, 64),
+                                       ("kda", 128, 128), ("kda", 32, 64)])
 def test_eager_step_matches_oracle(kind, P, N):
     sh = LayerShape(kind, 3, 5, P, N)
     cfg = rs.make_config(kind, "fp32", sh.B, sh.H, P, N, 16, 1)
@@ -53,7 +54,7 @@ def test_eager_step_matches_oracle(kind, P, N):
     assert float(rel_err(logical.cpu().numpy().reshape(-1, P, N), ses.S).max()) <= 1e-4
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_eager_snapshot_verify_matches_oracle(kind):
     sh = LayerShape(kind, 4, 3, 64, 128)
     T = 4
@@ -83,7 +84,7 @@ def test_eager_snapshot_verify_matches_oracle(kind):
     assert float(rel_err(logical.cpu().numpy().reshape(-1, sh.P, sh.N), ses.S).max()) <= 1e-4
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_replay_with_window_one_equals_eager(kind):
     """L = 1 folds every token (state written every step): replay and eager give the same outputs."""
     sh = LayerShape(kind, 2, 4, 64, 128)

@@ -30,7 +30,7 @@ def _layer(kind, sh, L, T, S0, precision="fp32"):
     return cfg, lay
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_accept_all_equals_standard_decoding(kind):
     sh = LayerShape(kind, 3, 4, 64, 128)
     T, L = 4, 12
@@ -86,7 +86,8 @@ def test_reject_all_changes_nothing_committed_and_reappend_is_clean():
     assert torch.equal(la.hp, lb.hp)
 
 
-@pytest.mark.parametrize("kind,precision", [("mamba2", "fp32"), ("mamba2", "fp32_hp_bf16_lp"), ("gdn", "fp32")])
+@pytest.mark.parametrize("kind,precision", [("mamba2", "fp32"), ("mamba2", "fp32_hp_bf16_lp"), ("gdn", "fp32"),
+                                             ("kda", "fp32")])
 def test_two_runs_are_bit_identical(kind, precision):
     sh = LayerShape(kind, 64, 16, 64, 128)
     T, L = 4, 16

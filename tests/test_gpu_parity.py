@@ -65,7 +65,7 @@ def test_gdn_standard(P, N, decay):
     _assert_clean(rep)
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 @pytest.mark.parametrize("T,L", [(1, 4), (2, 5), (3, 8), (4, 16), (8, 8), (5, 13)])
 def test_spec_rounds(kind, T, L):
     """Random accepted prefixes (0..T) including rejected drafts that get overwritten."""
@@ -75,7 +75,7 @@ def test_spec_rounds(kind, T, L):
     _assert_clean(rep)
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_explicit_flush_mid_run(kind):
     sh = LayerShape(kind, 3, 2, 64, 64)
     r = Runner(sh, 8, 4, wid=50, decay="slow")
@@ -100,7 +100,7 @@ def test_explicit_flush_mid_run(kind):
     assert r.report.max_rel <= TOL and r.report.max_rel_u <= TOL
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_wide_window_standard(kind):
     """L = 64 with one wavefront per workgroup: more records than lanes (serial decay path,
     staging tail loop, alpha tail)."""
@@ -111,7 +111,7 @@ def test_wide_window_standard(kind):
     assert rep.folds == 2 * 2
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_wide_window_spec(kind):
     sh = LayerShape(kind, 3, 2, 32, 32)
     r = Runner(sh, 56, 8, wid=61, decay="slow")
@@ -120,7 +120,7 @@ def test_wide_window_spec(kind):
 
 
 @pytest.mark.parametrize("kind,P,N,L", [("mamba2", 64, 128, 16), ("mamba2", 16, 16, 4), ("gdn", 128, 128, 5),
-                                        ("gdn", 32, 64, 64)])
+                                        ("gdn", 32, 64, 64), ("kda", 128, 128, 5), ("kda", 32, 64, 64)])
 def test_fused_decode_step(kind, P, N, L):
     """replayssm_decode_step = append + decode in one launch: same oracle bar, ring written by it."""
     sh = LayerShape(kind, 3, 5, P, N)
@@ -129,7 +129,7 @@ def test_fused_decode_step(kind, P, N, L):
     _assert_clean(rep)
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 @pytest.mark.parametrize("T,L", [(4, 16), (3, 5), (8, 8)])
 def test_fused_verify_step(kind, T, L):
     sh = LayerShape(kind, 4, 3, 64, 128)
@@ -138,7 +138,7 @@ def test_fused_verify_step(kind, T, L):
     _assert_clean(rep)
 
 
-@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 def test_fused_equals_unfused_bitwise(kind):
     """Same inputs through append+decode and through decode_step: identical bits everywhere."""
     sh = LayerShape(kind, 5, 4, 64, 128)
