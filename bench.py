@@ -51,7 +51,7 @@ POOL_BYTES_MAX = 8 << 30
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "replay_kernel_mamba2_decode_b256_pmc.md")
 KERNEL_SOURCES = ["ssm_decode_amd/csrc/replay.hip", "ssm_decode_amd/csrc/device.hpp",
-                  "ssm_decode_amd/csrc/internal.hpp"]
+                  "ssm_decode_amd/csrc/internal.hpp", "ssm_decode_amd/csrc/route.hpp"]
 
 
 def counter_traffic():
@@ -95,8 +95,14 @@ def parse():
 # byte model (algorithmic bytes: what the method must move, per head)
 # ----------------------------------------------------------------------------
 
+def delta_rule(kind):
+    """Kinds whose records carry a beta and whose drafts' corrections u replace v in the ring."""
+    return kind in ("gdn", "kda")
+
+
 def record_bytes(kind, P, N):
-    return 4 + 4 * N + 4 * P + (4 if kind == "gdn" else 0)
+    gate = 4 * N if kind == "kda" else 4  # a gate row per record for KDA, else one scalar
+    return gate + 4 * N + 4 * P + (4 if delta_rule(kind) else 0)
 
 
 def ckpt_read_bytes(precision, P, N, fold):
@@ -113,13 +119,13 @@ def replay_launch_bytes(kind, precision, P, N, h, T, fold, fused=False):
     """Bytes one head moves in one decode/verify launch with h committed records before it.
 
     A fused launch (append + decode / verify) also writes the drafts' records to the ring
-    (k, alpha and v for Mamba-2; k, alpha and beta for GDN, whose u is counted below)."""
+    (k, alpha and v for Mamba-2; k, alpha and beta for GDN and KDA, whose u is counted below)."""
     b = ckpt_read_bytes(precision, P, N, fold)
     b += (h + T) * record_bytes(kind, P, N)  # committed records and the drafts' own records
     if fused:
-        b += T * (record_bytes(kind, P, N) - (4 * P if kind == "gdn" else 0))
+        b += T * (record_bytes(kind, P, N) - (4 * P if delta_rule(kind) else 0))
     b += T * 4 * N + T * 4 * P  # q in, o out
-    if kind == "gdn":
+    if delta_rule(kind):
         b += T * 4 * P  # u written back into the ring
     if fold:
         b += ckpt_write_bytes(precision, P, N)
@@ -139,7 +145,7 @@ def append_bytes(kind, P, N, T, precision="fp32"):
 def eager_bytes(kind, P, N, T, snapshots):
     # load the state once, store it after every draft (snapshots) or once, plus inputs and outputs
     stores = T if snapshots else 1
-    per_tok = 4 + 4 * N + 4 * P + 4 * N + 4 * P + (4 if kind == "gdn" else 0)  # alpha,k,v,q,out(,beta)
+    per_tok = record_bytes(kind, P, N) + 4 * N + 4 * P  # alpha, k, v (, beta), q, out
     return 4 * P * N * (1 + stores) + T * per_tok
 
 
@@ -474,6 +480,8 @@ def cpu_baseline(synth, w, seed, seconds, threads=None):
         t0 = time.perf_counter()
         if sh.kind == "mamba2":
             oracle.mamba2_round(S, args["alpha"].reshape(nh, 1), args["k"], args["v"], args["q"], acc)
+        elif sh.kind == "kda":
+            oracle.kda_round(S, args["alpha"], args["beta"].reshape(nh, 1), args["k"], args["v"], args["q"], acc)
         else:
             oracle.gdn_round(S, args["alpha"].reshape(nh, 1), args["beta"].reshape(nh, 1), args["k"], args["v"],
                              args["q"], acc)
@@ -567,6 +575,19 @@ def main():
                        "two_precision_verify_T4_accepted_tokens_per_s": r3p["accepted_tokens"] / (r3p["ms"] * 1e-3),
                        "two_precision_verify_T4_kernel_gbs": r3p["kernel_gbs"],
                        "two_precision_verify_T4_avg_us": r3p["kernel_avg_us"]}
+        w5 = synth.WORKLOADS["kda_decode_b256"]
+        r5 = run_standard_decode(torch, rs, synth, w5, 256, 16, args.seed, fused=False)
+        r5f = run_standard_decode(torch, rs, synth, w5, 256, 16, args.seed, fused=True)
+        e5 = run_eager(torch, rs, synth, w5, 256, 16, args.seed)
+        r5s = run_spec(torch, rs, synth, w5, 64, 8, args.seed)
+        wl[w5.name] = {"tokens_per_s": r5["tokens"] / (r5["ms"] * 1e-3),
+                       "decode_kernel_gbs": r5["kernel_bytes"] / (r5["kernel_ms_total"] * 1e6),
+                       "decode_kernel_avg_us": r5["kernel_avg_us"],
+                       "fused_tokens_per_s": r5f["tokens"] / (r5f["ms"] * 1e-3),
+                       "fused_kernel_gbs": r5f["kernel_bytes"] / (r5f["kernel_ms_total"] * 1e6),
+                       "eager_tokens_per_s": e5["tokens"] / (e5["ms"] * 1e-3), "eager_gbs": e5["gbs"],
+                       "verify_T4_accepted_tokens_per_s": r5s["accepted_tokens"] / (r5s["ms"] * 1e-3),
+                       "verify_T4_kernel_gbs": r5s["kernel_gbs"], "verify_T4_avg_us": r5s["kernel_avg_us"]}
         w4 = synth.WORKLOADS["mamba2_2prec_b256"]
         r4 = {}
         for prec in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):
@@ -594,9 +615,12 @@ def main():
             one = cpu_baseline(synth, w, args.seed, args.cpu_seconds / 2, threads=1)
             g = synth.WORKLOADS["gdn_decode_b256"]
             gd = cpu_baseline(synth, g, args.seed, args.cpu_seconds / 2)
+            kd = synth.WORKLOADS["kda_decode_b256"]
+            kc = cpu_baseline(synth, kd, args.seed, args.cpu_seconds / 2)
             line["cpu_baseline"]["more"] = {
                 "one_core": {"value": one["value"], "cores": one["cores"], "sample": one["sample"]},
-                g.name: {"value": gd["value"], "cores": gd["cores"], "sample": gd["sample"]}}
+                g.name: {"value": gd["value"], "cores": gd["cores"], "sample": gd["sample"]},
+                kd.name: {"value": kc["value"], "cores": kc["cores"], "sample": kc["sample"]}}
     print(json.dumps(line), flush=True)
 
 
