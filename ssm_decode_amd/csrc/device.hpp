@@ -106,18 +106,49 @@ __device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-// Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups).
-__device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16, kWave);
-  x += __shfl_xor(x, 32, kWave);
-  return x;
+// Cross-lane sums without the LDS crossbar. Every step adds a lane's value to
+// its partner's, and both partners form the same sum (a + b and b + a are the
+// same float), so every lane of a group ends with bit-identical totals.
+//  - within a 16-lane row: DPP moves (quad_perm for partners 1 and 2 apart,
+//    row_half_mirror and row_mirror once the value is uniform over 4 and 8 lanes);
+//  - across rows: gfx950's v_permlane16_swap (row 0 <-> 1, 2 <-> 3) and
+//    v_permlane32_swap (lanes l <-> l + 32); with both operands the same value
+//    the two results are a lane's own value and its partner's.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+
+__device__ __forceinline__ float swap_add16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float swap_add32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups).
+__device__ __forceinline__ float sum_groups(float x) { return swap_add32(swap_add16(x)); }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 template <int WIDTH>
 __device__ __forceinline__ float sum_width(float x) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  static_assert(WIDTH >= 1 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "power of two up to 64");
+  if constexpr (WIDTH >= 2) x += dpp_move<dpp::kQuadXor1>(x);
+  if constexpr (WIDTH >= 4) x += dpp_move<dpp::kQuadXor2>(x);
+  if constexpr (WIDTH >= 8) x += dpp_move<dpp::kRowHalfMirror>(x);
+  if constexpr (WIDTH >= 16) x += dpp_move<dpp::kRowMirror>(x);
+  if constexpr (WIDTH >= 32) x = swap_add16(x);
+  if constexpr (WIDTH >= 64) x = swap_add32(x);
   return x;
 }
 

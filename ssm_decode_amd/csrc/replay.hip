@@ -617,6 +617,32 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   };
 
   // ---- 4/5. outputs of the drafts ---------------------------------------------
+  // Record r's factors for all drafts are one LDS row of TMAX floats (cq / ck row
+  // r, gq / gk row r + 1), read as whole rows so that a record costs one round
+  // trip for every draft. After the group sums every lane group holds every
+  // draft's value of its rows, so group g stores drafts g, g + 4: a wave writes
+  // its drafts with one store instead of one per draft.
+  auto row = [&](const float* p, float (&x)[TMAX]) {
+    if constexpr (TMAX == 1) {
+      x[0] = p[0];
+    } else {
+#pragma unroll
+      for (int c = 0; c < TMAX; c += 4) {
+        const f32x4 v = ld4(p + c);
+        x[c] = v[0];
+        x[c + 1] = v[1];
+        x[c + 2] = v[2];
+        x[c + 3] = v[3];
+      }
+    }
+  };
+  auto pick = [&](const float (&x)[TMAX], int i0) {
+    float r = x[i0];
+#pragma unroll
+    for (int c = 1; c < 4; ++c)
+      if (i0 + c < TMAX && g == c) r = x[i0 + c];
+    return r;
+  };
   auto write_outputs = [&]() {
   if (outputs) {
     const float* gq = sm + lds.gq;
@@ -624,63 +650,120 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     const float* cq = sm + lds.cq;
     const float* ck = sm + lds.ck;
     const float* sv = sm + lds.v + prow;
-    // decay factors of the output and correction sums (KDA: the gates are on the
-    // staged vectors and every factor is 1)
-    auto fq = [&](int idx) { return KDA ? 1.f : gq[idx]; };
-    auto fk = [&](int idx) { return KDA ? 1.f : gk[idx]; };
+    float* obase = a.out + ((int64_t)b * T * H + hd) * dv + prow;  // draft 0; draft i is i H dv further
+    const int64_t ostep = (int64_t)H * dv;
+    float oc[TMAX];
     if constexpr (!GDN) {
+      // every staged record r0 .. R - 1 in one pass; the decay rows are zero for
+      // records after a draft's end point
+      float q0[TMAX];
+      row(gq + r0 * TMAX, q0);
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i) {
-        if (i < T) {
-          float acc = gq[r0 * TMAX + i] * yq[i];
-          for (int r = r0 + g; r <= hc + i; r += 4)
-            acc += gq[(r + 1) * TMAX + i] * cq[r * TMAX + i] * sv[r * lds.dvs];
-          acc = sum_groups(acc);
-          if (g == 0) __builtin_nontemporal_store(acc, a.out + (((int64_t)b * T + i) * H + hd) * dv + prow);
+      for (int i = 0; i < TMAX; ++i) oc[i] = q0[i] * yq[i];
+      for (int r = r0 + g; r < R; r += 4) {
+        float w[TMAX], c[TMAX];
+        row(gq + (r + 1) * TMAX, w);
+        row(cq + r * TMAX, c);
+        const float u = sv[r * lds.dvs];
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) oc[i] += w[i] * c[i] * u;
+      }
+#pragma unroll
+      for (int i = 0; i < TMAX; ++i)
+        if (i < T) oc[i] = sum_groups(oc[i]);
+    } else {
+      // committed records in parallel over the four lane groups (KDA: every
+      // decay factor is 1, the gates being on the staged vectors)
+      float wc[TMAX];
+      if constexpr (KDA) {
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          wc[i] = yk[i];
+          oc[i] = yq[i];
+        }
+      } else {
+        float k0[TMAX], q0[TMAX];
+        row(gk + r0 * TMAX, k0);
+        row(gq + r0 * TMAX, q0);
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          wc[i] = k0[i] * yk[i];
+          oc[i] = q0[i] * yq[i];
         }
       }
-    } else {
-      // committed records in parallel over the four lane groups
-      float wc[TMAX], oc[TMAX];
+      for (int r = r0 + g; r < hc; r += 4) {
+        float kc[TMAX], qc[TMAX];
+        row(ck + r * TMAX, kc);
+        row(cq + r * TMAX, qc);
+        const float u = sv[r * lds.dvs];
+        if constexpr (!KDA) {
+          float kw[TMAX], qw[TMAX];
+          row(gk + (r + 1) * TMAX, kw);
+          row(gq + (r + 1) * TMAX, qw);
+#pragma unroll
+          for (int i = 0; i < TMAX; ++i) {
+            kc[i] *= kw[i];
+            qc[i] *= qw[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          wc[i] += kc[i] * u;
+          oc[i] += qc[i] * u;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TMAX; ++i) {
-        wc[i] = 0.f;
-        oc[i] = 0.f;
         if (i < T) {
-          wc[i] = fk(r0 * TMAX + i) * yk[i];
-          oc[i] = fq(r0 * TMAX + i) * yq[i];
-          for (int r = r0 + g; r < hc; r += 4) {
-            const float u = sv[r * lds.dvs];
-            wc[i] += fk((r + 1) * TMAX + i) * ck[r * TMAX + i] * u;
-            oc[i] += fq((r + 1) * TMAX + i) * cq[r * TMAX + i] * u;
-          }
           wc[i] = sum_groups(wc[i]);
           oc[i] = sum_groups(oc[i]);
         }
       }
-      // drafts in order: u_i needs the corrections of the drafts before it
+      // drafts in order: u_d needs the corrections of the drafts before it; once
+      // u_d is known it enters the sums of the drafts after it
       float ud[TMAX];
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i) {
-        ud[i] = 0.f;
-        if (i < T) {
-          float w = wc[i];
+      for (int d = 0; d < TMAX; ++d) {
+        ud[d] = 0.f;
+        if (d < T) {
+          const float al = KDA ? 1.f : sm[lds.alpha + hc + d];
+          const float be = sm[lds.beta + hc + d];
+          ud[d] = be * (sv[(hc + d) * lds.dvs] - al * wc[d]);
+          float kc[TMAX], qc[TMAX];
+          row(ck + (hc + d) * TMAX, kc);
+          row(cq + (hc + d) * TMAX, qc);
+          if constexpr (!KDA) {
+            float kw[TMAX], qw[TMAX];
+            row(gk + (hc + d + 1) * TMAX, kw);
+            row(gq + (hc + d + 1) * TMAX, qw);
 #pragma unroll
-          for (int d = 0; d < i; ++d) w += fk((hc + d + 1) * TMAX + i) * ck[(hc + d) * TMAX + i] * ud[d];
-          const float al = KDA ? 1.f : sm[lds.alpha + hc + i];
-          const float be = sm[lds.beta + hc + i];
-          ud[i] = be * (sv[(hc + i) * lds.dvs] - al * w);
-          float o = oc[i];
+            for (int j = d; j < TMAX; ++j) {
+              kc[j] *= kw[j];
+              qc[j] *= qw[j];
+            }
+          }
 #pragma unroll
-          for (int d = 0; d <= i; ++d) o += fq((hc + d + 1) * TMAX + i) * cq[(hc + d) * TMAX + i] * ud[d];
-          if (g == 0) {
-            __builtin_nontemporal_store(o, a.out + (((int64_t)b * T + i) * H + hd) * dv + prow);
-            int slot = head + hc + i;
-            if (slot >= C) slot -= C;
-            a.ring_v[(bh * C + slot) * dv + prow] = ud[i];
+          for (int j = d; j < TMAX; ++j) {
+            if (j > d) wc[j] += kc[j] * ud[d];
+            oc[j] += qc[j] * ud[d];
           }
         }
       }
+      // the drafts' corrections replace their v in the ring
+#pragma unroll
+      for (int i0 = 0; i0 < TMAX; i0 += 4) {
+        const int i = i0 + g;
+        if (i < T) {
+          int slot = head + hc + i;
+          if (slot >= C) slot -= C;
+          a.ring_v[(bh * C + slot) * dv + prow] = pick(ud, i0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i0 = 0; i0 < TMAX; i0 += 4) {
+      const int i = i0 + g;
+      if (i < T) __builtin_nontemporal_store(pick(oc, i0), obase + i * ostep);
     }
   }
   };
