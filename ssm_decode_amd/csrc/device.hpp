@@ -136,6 +136,30 @@ __device__ __forceinline__ float swap_add32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// DPP move whose lanes without a source lane (past the row end) get `fill`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move_fill(float x, float fill) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Product of x over lanes l .. 63, in every lane l. Within a 16-lane row a
+// doubling scan on row_shl (lane l reads lane l + d of its row; past the row
+// end it reads 1); then each row takes the totals of the rows after it, which
+// sit in their first lanes.
+__device__ __forceinline__ float suffix_product64(float x, int lane) {
+  x *= dpp_move_fill<0x101>(x, 1.f);  // row_shl:1
+  x *= dpp_move_fill<0x102>(x, 1.f);  // row_shl:2
+  x *= dpp_move_fill<0x104>(x, 1.f);  // row_shl:4
+  x *= dpp_move_fill<0x108>(x, 1.f);  // row_shl:8
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  const int row = lane >> 4;
+  const float tail = row == 0 ? r1 * (r2 * r3) : row == 1 ? r2 * r3 : row == 2 ? r3 : 1.f;
+  return x * tail;
+}
+
 // Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups).
 __device__ __forceinline__ float sum_groups(float x) { return swap_add32(swap_add16(x)); }
 

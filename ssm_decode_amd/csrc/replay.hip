@@ -424,12 +424,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         const int e = (job & 1) ? hc + i - 1 : hc + i;
         float* out = sm + ((job & 1) ? lds.gk : lds.gq) + i;
         const int r = first + lane;
-        float x = (r + 1 <= e) ? sm[lds.alpha + r + 1] : 1.f;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-          const float y = __shfl_down(x, d, kWave);
-          if (lane + d < kWave) x *= y;
-        }
+        const float x = suffix_product64((r + 1 <= e) ? sm[lds.alpha + r + 1] : 1.f, lane);
         if (r <= last) out[(r + 1) * TMAX] = (r <= e) ? x : 0.f;
       }
     } else {
@@ -585,13 +580,8 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     // (KDA: the column decay is already applied and the keys carry the rest)
     float gf = 1.f;
     if constexpr (!KDA) {
-      gf = (lane < hc) ? sm[lds.alpha + lane] : 1.f;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const float y = __shfl_down(gf, d, kWave);
-        if (lane + d < kWave) gf *= y;
-      }
-      const float G = __shfl(gf, 0, kWave);
+      gf = suffix_product64((lane < hc) ? sm[lds.alpha + lane] : 1.f, lane);
+      const float G = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gf), 0));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) S[nt] *= G;
     }
