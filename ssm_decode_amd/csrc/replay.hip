@@ -115,6 +115,12 @@ struct StageMap {
   }
 };
 
+// A work item: its index and its (sequence, head), stepped along with the
+// index so that no item divides by H.
+struct Item {
+  int id, b, hd;
+};
+
 // Source rows of one item: committed records from the ring; the drafts from
 // the ring too, or, in a fused call, straight from the caller's inputs.
 struct RowSrc {
@@ -128,10 +134,10 @@ struct RowSrc {
 };
 
 template <int NT>
-__device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) {
+__device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, const Item& it, int T) {
   constexpr int DK = NT * 16;
   const int H = a.H, C = a.C, dv = a.dv;
-  const int b = item / H, hd = item - b * H;
+  const int b = it.b, hd = it.hd;
   const int64_t bh = (int64_t)b * H + hd;
   RowSrc s;
   s.rk = a.ring_k + bh * (int64_t)C * DK;
@@ -145,16 +151,18 @@ __device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, int item, int T) 
 }
 
 template <int KIND, int NT, int TMAX, bool FUSED>
-__device__ __forceinline__ void load_records(const ReplayArgs& a, int item, const SeqPtr& p, const Route& rt,
-                                             bool valid, int tid, const StageMap& m, RecRegs<TMAX>& rr) {
+__device__ __forceinline__ void load_records(const ReplayArgs& a, const Item& item, const SeqPtr& p,
+                                             const Route& rt, bool valid, int tid, const StageMap& m,
+                                             RecRegs<TMAX>& rr) {
   constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
   constexpr int DK = NT * 16;
   // Every load is issued; one with nothing to fetch reads the first element of a
   // ring array (always allocated: q and the inputs are NULL in a flush call).
   const bool ok = valid && rt.work;
   const int H = a.H, C = a.C, dv = a.dv, T = ok ? rt.T : 0, R = ok ? rt.R : 0;
-  const int b = ok ? item / H : 0, hd = ok ? item - b * H : 0;
-  const RowSrc s = row_src<NT>(a, ok ? item : 0, T);
+  const Item it = ok ? item : Item{0, 0, 0};
+  const int b = it.b, hd = it.hd;
+  const RowSrc s = row_src<NT>(a, it, T);
   constexpr bool fused = FUSED;
 #pragma unroll
   for (int j = 0; j < kRecK; ++j) {
@@ -197,15 +205,15 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, int item, cons
 // A fused call also writes the drafts' records into their ring slots (k,
 // alpha, and v for Mamba-2 / beta for GDN, whose u replaces v later).
 template <int KIND, int NT, int TMAX, bool FUSED>
-__device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds, int item,
-                                              const SeqPtr& p, const Route& rt, int tid, int nthr,
-                                              const StageMap& m, const RecRegs<TMAX>& rr) {
+__device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds,
+                                              const Item& item, const SeqPtr& p, const Route& rt, int tid,
+                                              int nthr, const StageMap& m, const RecRegs<TMAX>& rr) {
   constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
   constexpr int DK = NT * 16;
   constexpr bool GDN = kind_gdn(KIND);
   const bool raw = exact_fold<KIND>(rt);
   const int H = a.H, C = a.C, dv = a.dv, T = rt.T, R = rt.R;
-  const int b = item / H, hd = item - b * H;
+  const int b = item.b, hd = item.hd;
   const RowSrc s = row_src<NT>(a, item, T);
   constexpr bool fused = FUSED;
   float* wk = a.ring_k + (s.rk - a.ring_k);
@@ -290,9 +298,10 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
 // item. On return rr holds (or is loading) the rows of `next` and S its
 // checkpoint copy. Ends with a workgroup barrier after its last LDS read.
 template <int KIND, int NT, int TMAX, bool FUSED>
-__device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const int item, const SeqPtr ptr,
-                                            const Route rt, f32x4 (&S)[NT], RecRegs<TMAX>& rr, const int next,
-                                            const SeqPtr nptr, const Route nrt) {
+__device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const ReplayLds& lds,
+                                            const StageMap& map0, const Item it, const SeqPtr ptr, const Route rt,
+                                            f32x4 (&S)[NT], RecRegs<TMAX>& rr, const Item nit, const SeqPtr nptr,
+                                            const Route nrt) {
   constexpr int DK = NT * 16;
   constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
   constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
@@ -311,12 +320,13 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int g = lane >> 4;
   const int col = lane & 15;
   const int H = a.H, C = a.C, dv = a.dv;
-  const int b = item / H;
-  const int hd = item - b * H;
+  const int b = it.b;
+  const int hd = it.hd;
   const int64_t bh = (int64_t)b * H + hd;
   const int prow = wave * 16 + col;  // the state row this lane owns
-  const ReplayLds lds(C, DK, dv, TMAX, KIND);
-  const StageMap map(tid, nthr, LPR, dv);
+  // (the staging map is computed once per workgroup and laundered like tid)
+  StageMap map = map0;
+  __asm__ volatile("" : "+v"(map.rk0), "+v"(map.ck), "+v"(map.rv0), "+v"(map.cv));
 
   const int mode = a.mode;
   const int prec = a.precision;
@@ -331,12 +341,12 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int R = rt.R, r0 = rt.r0;
 
   // ---- 1. records (the checkpoint copy is already in flight) --------------------
-  if (work) store_records<KIND, NT, TMAX, FUSED>(a, sm, lds, item, ptr, rt, tid, nthr, map, rr);
+  if (work) store_records<KIND, NT, TMAX, FUSED>(a, sm, lds, it, ptr, rt, tid, nthr, map, rr);
   __syncthreads();
 
   // ---- the next item's ring rows: requested now, waited for by the next item
-  const bool more = next < a.B * a.H;
-  load_records<KIND, NT, TMAX, FUSED>(a, next, nptr, nrt, more, tid, map, rr);
+  const bool more = nit.id < a.B * a.H;
+  load_records<KIND, NT, TMAX, FUSED>(a, nit, nptr, nrt, more, tid, map, rr);
 
   // ---- KDA: the gate products, per channel (a thread per channel and job) ------
   // With per-channel gates the state after records [0, m] is
@@ -379,7 +389,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   auto prefetch_next = [&]() {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) __asm__ volatile("" ::"v"(S[nt]));
-    prefetch_ckpt<NT>(a, next, nrt.fold, more && nrt.work, wave, lane, S);
+    prefetch_ckpt<NT>(a, nit.id, nrt.fold, more && nrt.work, wave, lane, S);
   };
   const bool lp = reads_lp(prec, fold);
 
@@ -857,18 +867,33 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   if (!any) rt.work = false;
   f32x4 S[NT];
   RecRegs<TMAX> rr;
-  {
-    const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
-    load_records<KIND, NT, TMAX, FUSED>(a, blockIdx.x, ptr, rt, any, threadIdx.x, map, rr);
-  }
-  prefetch_ckpt<NT>(a, blockIdx.x, rt.fold, any && rt.work, wave, lane, S);
-  for (int k = 0, item = blockIdx.x; item < items; ++k, item += G) {
-    const int next = item + G;
+  // Loop invariants of the workgroup: the LDS carve-up and where a thread's
+  // share of the ring rows lies.
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
+  const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
+  // Items advance by the grid size G: (sequence, head) advances by (G / H, G % H)
+  // with a carry, so no item divides by H.
+  const int H = a.H;
+  const int step_b = G / H, step_h = G - step_b * H;
+  auto advance = [&](const Item& x) {
+    Item n{x.id + G, x.b + step_b, x.hd + step_h};
+    if (n.hd >= H) {
+      n.hd -= H;
+      ++n.b;
+    }
+    return n;
+  };
+  Item it{(int)blockIdx.x, (int)blockIdx.x / H, (int)blockIdx.x % H};
+  load_records<KIND, NT, TMAX, FUSED>(a, it, ptr, rt, any, threadIdx.x, map, rr);
+  prefetch_ckpt<NT>(a, it.id, rt.fold, any && rt.work, wave, lane, S);
+  for (int k = 0; it.id < items; ++k) {
+    const Item nit = advance(it);
     const int kn = (k + 1) & 63;
-    if (kn == 0 && next < items) batch(next);
+    if (kn == 0 && nit.id < items) batch(nit.id);
     const SeqPtr nptr = ptr_at(kn);
     const Route nrt = route_of(a, nptr);
-    replay_item<KIND, NT, TMAX, FUSED>(a, sm, item, ptr, rt, S, rr, next, nptr, nrt);
+    replay_item<KIND, NT, TMAX, FUSED>(a, sm, lds, map, it, ptr, rt, S, rr, nit, nptr, nrt);
+    it = nit;
     ptr = nptr;
     rt = nrt;
   }
