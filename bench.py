@@ -496,7 +496,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path has no cross-GPU step (sequences and heads shard "
-              "with no exchange), and this build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+              "with no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -1,4 +1,4 @@
-"""Lock-step driver of the GPU path (through the C ABI) and the CPU oracle.
+"""Lock-step runner of the GPU path (through the C ABI) and the CPU oracle.
 
 The GPU runs the whole layer; the oracle follows every head, or a sample of
 heads of a full-size layer (heads are independent, so a sample is followed
