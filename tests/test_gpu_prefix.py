@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("kind,precision", [("mamba2", "fp32"), ("mamba2", "fp32_hp_bf16_lp"),
-                                            ("gdn", "fp32"), ("gdn", "fp32_hp_bf16_lp")])
+                                            ("gdn", "fp32"), ("gdn", "fp32_hp_bf16_lp"), ("kda", "fp32")])
 def test_snapshot_after_selective_flush_is_the_exact_state(kind, precision):
     """After 11 standard steps (L = 8: 3 records unfolded) a selective flush of sequences 0 and 2
     makes their checkpoints the state after all 11 tokens: the snapshot equals the oracle's
@@ -55,7 +55,7 @@ def test_snapshot_of_a_stale_sequence_is_flagged():
 
 
 @pytest.mark.parametrize("kind,precision", [("mamba2", "fp32"), ("mamba2", "fp32_hp_bf16_lp"), ("gdn", "fp32"),
-                                            ("gdn", "fp32_hp_bf16_lp")])
+                                            ("gdn", "fp32_hp_bf16_lp"), ("kda", "fp32")])
 def test_restored_sequences_continue_like_their_source(kind, precision):
     """Sequence 0 is flushed and snapshot; sequences 2 and 3 are restored from it. Fed the same
     tokens as sequence 0 from then on, they give bit-identical outputs and checkpoints."""
