@@ -89,7 +89,7 @@ typedef struct replayssm_config {
   int32_t kind;      /* enum replayssm_kind                                        */
   int32_t precision; /* enum replayssm_precision                                   */
   int32_t B;         /* sequences, >= 1                                            */
-  int32_t H;         /* heads per sequence, >= 1, B*H < 2^31                       */
+  int32_t H;         /* heads per sequence, >= 1, B*H <= 2^30                      */
   int32_t dv;        /* 16..256, multiple of 16                                    */
   int32_t dk;        /* 16, 32, 64 or 128 (32, 64, 128 when a bf16 copy is kept)   */
   int32_t L;         /* window: records folded per checkpoint write, 1..64          */

@@ -60,7 +60,8 @@ int check_config(const replayssm_config* c) {
     return fail(REPLAYSSM_EINVAL, "precision %d unknown", c->precision);
   if (c->B < 1 || c->B > 65535) return fail(REPLAYSSM_EINVAL, "B=%d outside 1..65535", c->B);
   if (c->H < 1) return fail(REPLAYSSM_EINVAL, "H=%d < 1", c->H);
-  if ((int64_t)c->B * c->H >= (int64_t)1 << 31) return fail(REPLAYSSM_EINVAL, "B*H too large");
+  // (item indices plus the grid stride stay below 2^31)
+  if ((int64_t)c->B * c->H > (int64_t)1 << 30) return fail(REPLAYSSM_EINVAL, "B*H above 2^30");
   if (c->dv < 16 || c->dv > rs::kMaxDv || c->dv % 16 != 0)
     return fail(REPLAYSSM_EINVAL, "dv=%d must be a multiple of 16 in 16..256", c->dv);
   if (c->dk != 16 && c->dk != 32 && c->dk != 64 && c->dk != 128)
