@@ -67,6 +67,9 @@ int check_config(const replayssm_config* c) {
   if (c->dk != 16 && c->dk != 32 && c->dk != 64 && c->dk != 128)
     return fail(REPLAYSSM_EINVAL, "dk=%d must be 16, 32, 64 or 128", c->dk);
   if (c->L < 1 || c->L > rs::kMaxL) return fail(REPLAYSSM_EINVAL, "L=%d outside 1..64", c->L);
+  // one sequence's appended rows are counted in 32-bit float4 units
+  if ((int64_t)c->H * 8 * (2 * c->dk + c->dv) / 4 > (int64_t)1 << 30)
+    return fail(REPLAYSSM_EINVAL, "H=%d too large for one sequence's records", c->H);
   if (c->T_max < 1 || c->T_max > rs::kMaxDrafts || c->T_max > c->L)
     return fail(REPLAYSSM_EINVAL, "T_max=%d outside 1..min(8, L)", c->T_max);
   if (c->precision != REPLAYSSM_FP32 && c->dk % 32 != 0)

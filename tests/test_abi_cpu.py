@@ -79,7 +79,7 @@ def test_window_sweep_configs_fit(rs, L, T):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(kind=5), -1), (dict(precision=7), -1), (dict(B=0), -1), (dict(B=70000), -1), (dict(H=0), -1), (dict(B=65535, H=16385), -1),
+    (dict(kind=5), -1), (dict(precision=7), -1), (dict(B=0), -1), (dict(B=70000), -1), (dict(H=0), -1), (dict(B=65535, H=16385), -1), (dict(B=1, H=1 << 21), -1),
     (dict(dv=24), -1), (dict(dv=272), -1), (dict(dk=48), -1), (dict(dk=256), -1), (dict(L=0), -1),
     (dict(L=65), -1), (dict(T_max=0), -1), (dict(T_max=9, L=16), -1), (dict(T_max=5, L=4), -1),
     (dict(precision="fp32_hp_bf16_lp", dk=16, dv=16), -2), (dict(kind="gdn", precision="bf16_shared"), -2),
