@@ -173,10 +173,11 @@ def make_pool(torch, synth, shape, T, n_needed, seed, wid, bytes_per_set):
     return [synth.device_step(seed, wid, 1000 + i, shape, T, "cuda") for i in range(n)]
 
 
-def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True, fused=True):
+def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True, fused=True, precision=None):
     """Standard-decoding steps (fused append + decode launches, or append then decode)."""
     sh = w.shape
-    cfg = rs.make_config(sh.kind, w.precision, sh.B, sh.H, sh.P, sh.N, w.L, 1)
+    prec = precision or w.precision
+    cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, 1)
     layer = rs.LayerState(cfg)
     layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
     rb = record_bytes(sh.kind, sh.P, sh.N)
@@ -203,11 +204,11 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
     h, kbytes, nfold = h0, 0, 0
     for _ in range(steps):
         fold = h + 1 > w.L
-        kbytes += replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold, fused)
+        kbytes += replay_launch_bytes(sh.kind, prec, sh.P, sh.N, h, 1, fold, fused)
         nfold += fold
         h = 1 if fold else h + 1
     res = {"ms": tm.ms, "steps": steps, "tokens": sh.B * steps, "decode_bytes": kbytes * sh.B * sh.H,
-           "append_bytes": 0 if fused else append_bytes(sh.kind, sh.P, sh.N, 1, w.precision) * sh.B * sh.H * steps,
+           "append_bytes": 0 if fused else append_bytes(sh.kind, sh.P, sh.N, 1, prec) * sh.B * sh.H * steps,
            "folds": nfold, "fused": fused}
     if kernel_pass:
         # second pass: events around every decode launch (same stream as the kernels)
@@ -230,7 +231,7 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
         h, kb, fold_ms, plain_ms, fold_b, plain_b = h1, 0, [], [], 0, 0
         for i in range(steps):
             fold = h + 1 > w.L
-            bb = replay_launch_bytes(sh.kind, w.precision, sh.P, sh.N, h, 1, fold, fused) * sh.B * sh.H
+            bb = replay_launch_bytes(sh.kind, prec, sh.P, sh.N, h, 1, fold, fused) * sh.B * sh.H
             kb += bb
             (fold_ms if fold else plain_ms).append(durs[i])
             if fold:
@@ -450,6 +451,19 @@ def ceilings(torch, rs):
                           "non-temporal 16-byte loads)", "d2d_copy": "torch copy_ of 2 GiB (hipMemcpy D2D)"}
 
 
+def host_cpu():
+    """CPU model and the cores this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(synth, w, seed, seconds, threads=None):
     """The oracle as it stands, on a bounded sample of the workload: B' sequences (all heads)."""
     import oracle
@@ -488,6 +502,7 @@ def cpu_baseline(synth, w, seed, seconds, threads=None):
         spent += time.perf_counter() - t0
         steps += 1
     return {"value": Bs * steps / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"{Bs} of {sh.B} sequences (all {sh.H} heads), {steps} decode steps, fp64 eager "
                       f"recurrence, {spent:.1f} s of oracle time (input generation excluded)"}
 
@@ -547,6 +562,14 @@ def main():
                          "kernel_gbs": fu["kernel_bytes"] / (fu["kernel_ms_total"] * 1e6),
                          "kernel_avg_us": fu["kernel_avg_us"],
                          "step": "replayssm_decode_step (append + decode in one launch)"}
+    if not args.quick:
+        tp = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False,
+                                 precision="fp32_hp_bf16_lp")
+        line["two_precision"] = {"tokens_per_s": tp["tokens"] / (tp["ms"] * 1e-3),
+                                 "kernel_gbs": tp["kernel_bytes"] / (tp["kernel_ms_total"] * 1e6),
+                                 "kernel_avg_us": tp["kernel_avg_us"], "plain_step_us": tp["plain_avg_us"],
+                                 "fold_step_us": tp["fold_avg_us"],
+                                 "step": "replayssm_append then replayssm_decode, bf16 copy read off-fold"}
     if not args.quick:
         eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
         line["eager"] = {"tokens_per_s": eg["tokens"] / (eg["ms"] * 1e-3), "gbs": eg["gbs"],

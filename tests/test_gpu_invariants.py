@@ -110,3 +110,30 @@ def test_two_runs_are_bit_identical(kind, precision):
     assert torch.equal(hp_a, hp_b)
     assert torch.equal(rv_a, rv_b)
     assert p_a == p_b
+
+
+@pytest.mark.parametrize("kind,precision", [("mamba2", "fp32"), ("mamba2", "fp32_hp_bf16_lp"), ("gdn", "fp32"),
+                                            ("gdn", "fp32_hp_bf16_lp"), ("kda", "fp32")])
+def test_checkpoint_written_once_per_window(kind, precision):
+    """Standard decoding writes the checkpoint only on fold steps: across every other call its
+    bytes (both copies) are bitwise unchanged, and L = 4 gives one write per 4 tokens after the
+    first window (folds at tokens 5, 9, 13, ...)."""
+    sh = LayerShape(kind, 3, 2, 64, 128)
+    L, steps = 4, 17
+    S0 = torch.from_numpy(host_initial_state(7, 93, sh, 0.1)).cuda()
+    cfg, lay = _layer(kind, sh, L, 1, S0, precision)
+    out = torch.empty((sh.B, sh.H, sh.P), device="cuda")
+    writes = []
+    for t in range(steps):
+        x = _x(7, 93, t, sh, 1)
+        before = [c.clone() for c in (lay.hp, lay.lp) if c is not None]
+        h_before = lay.h.tolist()
+        rs.decode_step(cfg, lay.struct, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out)
+        after = [c for c in (lay.hp, lay.lp) if c is not None]
+        changed = [not torch.equal(b, a) for b, a in zip(before, after)]
+        fold = h_before[0] + 1 > L
+        assert all(c == fold for c in changed), (t, h_before, changed)
+        if fold:
+            writes.append(t)
+    assert writes == [4, 8, 12, 16]
+    assert rs.read_error(lay.struct) == 0
