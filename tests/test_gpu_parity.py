@@ -56,7 +56,7 @@ def test_mamba2_long_run_slow_decay(decay):
     assert rep.folds == 2 * 7
 
 
-@pytest.mark.parametrize("P,N", [(128, 128), (32, 64), (16, 16)])
+@pytest.mark.parametrize("P,N", [(128, 128), (32, 64), (16, 16), (256, 32), (256, 128)])
 @pytest.mark.parametrize("decay", ["recipe", "slow"])
 def test_gdn_standard(P, N, decay):
     sh = LayerShape("gdn", 2, 3, P, N)
@@ -157,3 +157,15 @@ def test_fused_equals_unfused_bitwise(kind):
         assert torch.equal(oa, ob), t
     assert torch.equal(la.hp, lb.hp) and torch.equal(la.ring_k, lb.ring_k) and torch.equal(la.ring_v, lb.ring_v)
     assert torch.equal(la.ring_alpha, lb.ring_alpha) and la.pointers() == lb.pointers()
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
+@pytest.mark.parametrize("P,N,T,L", [(256, 128, 4, 12), (256, 64, 8, 8), (48, 128, 3, 7)])
+def test_spec_rounds_wide_and_odd_heads(kind, P, N, T, L):
+    """16 wavefronts per workgroup (dv = 256) and an odd tile count (dv = 48), speculative rounds
+    with random accepted prefixes and folds."""
+    sh = LayerShape(kind, 3, 2, P, N)
+    r = Runner(sh, L, T, wid=130 + T, decay="slow")
+    rep = run_spec(r, T, 20)
+    _assert_clean(rep)
+    assert rep.folds > 0
