@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
     ap.add_argument("--window-sweep", action="store_true", help="also run the window-size sweep L x T")
+    ap.add_argument("--flush-only", action="store_true",
+                    help="only the standalone flush leg (replayssm_flush folding L records per head); for profiling")
     return ap.parse_args()
 
 
@@ -345,6 +347,62 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
     return res
 
 
+def flush_launch_bytes(kind, precision, P, N, h):
+    """Bytes one head moves in a replayssm_flush launch that folds h committed records: the
+    checkpoint copy the fold reads, the h records, and the checkpoint copies it writes."""
+    b = ckpt_read_bytes(precision, P, N, True) + h * record_bytes(kind, P, N) + ckpt_write_bytes(precision, P, N)
+    # GDN with the two-precision checkpoint stages the raw v rows and beta (to recompute the
+    # corrections) in place of the stored u; every other delta-rule fold stages no beta
+    if delta_rule(kind) and not (kind == "gdn" and precision == "fp32_hp_bf16_lp"):
+        b -= h * 4
+    return b
+
+
+def run_flush(torch, rs, synth, w, cycles, warmup, seed, precision=None):
+    """Standalone checkpoint folds: every cycle is L standard decoding steps (append + decode; the
+    window fills without a fold) followed by one replayssm_flush, which folds all L committed
+    records of every sequence (rank-L update per head). Only the flush launches are timed, with
+    events on the kernels' stream."""
+    sh = w.shape
+    prec = precision or w.precision
+    cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, 1)
+    layer = rs.LayerState(cfg)
+    layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
+    rb = record_bytes(sh.kind, sh.P, sh.N)
+    pool = make_pool(torch, synth, sh, 1, w.L * 4, seed, w.wid, sh.B * sh.H * (rb + 4 * (sh.N + sh.P)))
+    out = torch.empty((sh.B, sh.H, sh.P), dtype=torch.float32, device="cuda")
+    st, stream = layer.struct, torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cycles)]
+    n = 0
+    for c in range(warmup + cycles):
+        for _ in range(w.L):
+            x = pool[n % len(pool)]
+            n += 1
+            rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+            rs.decode(cfg, st, x["q"], out, stream)
+        if c >= warmup:
+            evs[c - warmup][0].record(stream)
+        rs.flush(cfg, st, stream)
+        if c >= warmup:
+            evs[c - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    h = int(layer.h[0].item())
+    err = rs.read_error(st)
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    if h != 0:
+        raise RuntimeError(f"flush left h = {h}")
+    durs = np.array([a.elapsed_time(b) for a, b in evs])
+    us = float(durs.mean() * 1e3)
+    nbytes = flush_launch_bytes(sh.kind, prec, sh.P, sh.N, w.L) * sh.B * sh.H
+    flops = 2 * sh.P * sh.N * w.L * sh.B * sh.H  # V diag(gamma) K^T over the L folded records
+    del layer, pool
+    return {"launches": cycles, "records_folded_per_head": w.L, "avg_us": us, "min_us": float(durs.min() * 1e3),
+            "bytes_per_launch": nbytes, "gbs": nbytes / (us * 1e3), "hbm_frac": nbytes / (us * 1e3) / HBM_PEAK_GBS,
+            "flops_per_launch": flops, "tflops": flops / (us * 1e6),
+            "mfma_frac": flops / (us * 1e6) / MFMA_F32_PEAK_TFLOPS, "precision": prec}
+
+
 def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
     sh = w.shape
     cfg = rs.make_config(sh.kind, "fp32", sh.B, sh.H, sh.P, sh.N, w.L, T)
@@ -464,20 +522,21 @@ def host_cpu():
     return {"model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(synth, w, seed, seconds, threads=None):
-    """The oracle as it stands, on a bounded sample of the workload: B' sequences (all heads)."""
+def cpu_baseline(synth, w, seed, seconds, threads=None, seqs=64):
+    """The oracle as it stands, on a bounded sample of the workload: `seqs` sequences (all heads),
+    as many of the workload's 512 steps as fit in about `seconds` of oracle time."""
     import oracle
 
     if threads is not None:
         prev = oracle.num_threads()
         oracle.set_num_threads(threads)
         try:
-            return cpu_baseline(synth, w, seed, seconds)
+            return cpu_baseline(synth, w, seed, seconds, seqs=seqs)
         finally:
             oracle.set_num_threads(prev)
 
     sh = w.shape
-    Bs = 64
+    Bs = min(seqs, sh.B)
     sub = synth.LayerShape(sh.kind, Bs, sh.H, sh.P, sh.N)
     nh = Bs * sh.H
     S = synth.host_initial_state(seed, w.wid, sub, w.s0_sigma).reshape(nh, sh.P, sh.N).astype(np.float64)
@@ -522,6 +581,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]
     sh = w.shape
+    if args.flush_only:
+        print(json.dumps({"flush": run_flush(torch, rs, synth, w, 16, 2, args.seed)}), flush=True)
+        return
     main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed, fused=False)
     fold_flops = 2 * sh.P * sh.N * w.L * sh.B * sh.H  # V diag(gamma) K^T over the L folded records
     tok_s = main_res["tokens"] / (main_res["ms"] * 1e-3)
@@ -611,6 +673,12 @@ def main():
                        "eager_tokens_per_s": e5["tokens"] / (e5["ms"] * 1e-3), "eager_gbs": e5["gbs"],
                        "verify_T4_accepted_tokens_per_s": r5s["accepted_tokens"] / (r5s["ms"] * 1e-3),
                        "verify_T4_kernel_gbs": r5s["kernel_gbs"], "verify_T4_avg_us": r5s["kernel_avg_us"]}
+        fl = {"mamba2_fp32": run_flush(torch, rs, synth, w, 16, 2, args.seed),
+              "mamba2_fp32_hp_bf16_lp": run_flush(torch, rs, synth, w, 16, 2, args.seed, precision="fp32_hp_bf16_lp"),
+              "gdn_fp32": run_flush(torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], 16, 2, args.seed),
+              "gdn_fp32_hp_bf16_lp": run_flush(torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], 16, 2,
+                                               args.seed, precision="fp32_hp_bf16_lp")}
+        line["flush"] = fl
         w4 = synth.WORKLOADS["mamba2_2prec_b256"]
         r4 = {}
         for prec in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):
@@ -633,7 +701,7 @@ def main():
     if args.window_sweep:
         line["window_sweep"] = window_sweep(torch, rs, synth, args.seed)
     if not (args.quick or args.no_cpu_baseline):
-        line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds, seqs=sh.B)
         if not args.quick:
             one = cpu_baseline(synth, w, args.seed, args.cpu_seconds / 2, threads=1)
             g = synth.WORKLOADS["gdn_decode_b256"]
