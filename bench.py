@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
     ap.add_argument("--window-sweep", action="store_true", help="also run the window-size sweep L x T")
+    ap.add_argument("--leg", choices=sorted(LEGS),
+                    help="run one benchmark leg only and print its figures (for profiling)")
     ap.add_argument("--flush-only", action="store_true",
                     help="only the standalone flush leg (replayssm_flush folding L records per head); for profiling")
     return ap.parse_args()
@@ -566,6 +568,34 @@ def cpu_baseline(synth, w, seed, seconds, threads=None, seqs=64):
                       f"recurrence, {spent:.1f} s of oracle time (input generation excluded)"}
 
 
+# Single legs (--leg NAME), each on its own workload: K steps or rounds after W warm-up ones.
+LEGS = {
+    "mamba2_decode": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=False),
+    "mamba2_decode_fused": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=True),
+    "mamba2_spec": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["mamba2_spec_b256"], k, w, seed),
+    "mamba2_decode_two_precision": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=False,
+        precision="fp32_hp_bf16_lp"),
+    "mamba2_spec_two_precision": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["mamba2_2prec_b256"], k, w, seed, precision="fp32_hp_bf16_lp"),
+    "mamba2_spec_bf16_shared": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["mamba2_2prec_b256"], k, w, seed, precision="bf16_shared"),
+    "gdn_decode": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], k, w, seed, fused=False),
+    "gdn_spec": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], k, w, seed),
+    "gdn_spec_two_precision": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], k, w, seed, precision="fp32_hp_bf16_lp"),
+    "kda_decode": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["kda_decode_b256"], k, w, seed, fused=False),
+    "kda_spec": lambda torch, rs, synth, k, w, seed: run_spec(
+        torch, rs, synth, synth.WORKLOADS["kda_decode_b256"], k, w, seed),
+}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -583,6 +613,10 @@ def main():
     sh = w.shape
     if args.flush_only:
         print(json.dumps({"flush": run_flush(torch, rs, synth, w, 16, 2, args.seed)}), flush=True)
+        return
+    if args.leg:
+        res = LEGS[args.leg](torch, rs, synth, args.steps, args.warmup, args.seed)
+        print(json.dumps({"leg": args.leg, **{k: v for k, v in res.items() if not isinstance(v, dict)}}), flush=True)
         return
     main_res = run_standard_decode(torch, rs, synth, w, args.steps, args.warmup, args.seed, fused=False)
     fold_flops = 2 * sh.P * sh.N * w.L * sh.B * sh.H  # V diag(gamma) K^T over the L folded records

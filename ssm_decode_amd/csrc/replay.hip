@@ -636,11 +636,21 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       }
     }
   };
+  // Lane group g's draft i0 + g, by selects on registers. Each candidate is
+  // laundered first: left as plain array reads, the select chain is folded into
+  // a lane-dependent index, which sends the array to scratch memory, and the
+  // scratch load's wait then drains every outstanding load, the next item's
+  // checkpoint prefetch included.
   auto pick = [&](const float (&x)[TMAX], int i0) {
     float r = x[i0];
 #pragma unroll
-    for (int c = 1; c < 4; ++c)
-      if (i0 + c < TMAX && g == c) r = x[i0 + c];
+    for (int c = 1; c < 4; ++c) {
+      if (i0 + c < TMAX) {
+        float xc = x[i0 + c];
+        __asm__ volatile("" : "+v"(xc));
+        r = (g == c) ? xc : r;
+      }
+    }
     return r;
   };
   auto write_outputs = [&]() {
