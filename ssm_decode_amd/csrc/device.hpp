@@ -103,6 +103,15 @@ __device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
+// acc + a . b as a chain of four fused multiply-adds (one instruction per
+// product: no separate add of a dot4 result)
+__device__ __forceinline__ float fma4(const f32x4& a, const f32x4& b, float acc) {
+  acc = __builtin_fmaf(a[0], b[0], acc);
+  acc = __builtin_fmaf(a[1], b[1], acc);
+  acc = __builtin_fmaf(a[2], b[2], acc);
+  return __builtin_fmaf(a[3], b[3], acc);
+}
+
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 

@@ -410,8 +410,8 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         if (i < T) {
           const float* qi = KDA ? sm + lds.qg + i * DK : sm + lds.q + i * DK;
           const float* ki = KDA ? sm + lds.kg + i * DK : sm + lds.k + (hc + i) * lds.dks;
-          yq[i] += dot4(S[nt], ld4(qi + nt * 16 + 4 * g));
-          if (GDN) yk[i] += dot4(S[nt], ld4(ki + nt * 16 + 4 * g));
+          yq[i] = fma4(S[nt], ld4(qi + nt * 16 + 4 * g), yq[i]);
+          if (GDN) yk[i] = fma4(S[nt], ld4(ki + nt * 16 + 4 * g), yk[i]);
         }
       }
     }
@@ -540,7 +540,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         const float* kj = sm + lds.k + (jj < nb ? j0 + jj : 0) * lds.dks + 4 * g;
         float part = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) part += dot4(S[nt], ld4(kj + 16 * nt));
+        for (int nt = 0; nt < NT; ++nt) part = fma4(S[nt], ld4(kj + 16 * nt), part);
         w0[jj] = part;
       }
 #pragma unroll
