@@ -195,6 +195,25 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
                      const float* alpha, const float* k, const float* v, const float* beta,
                      void* stream);
 
+/* replayssm_append with each record's decay computed on the GPU from the raw
+ * time step instead of passed in: the discretisation of the layer just before
+ * the path (Mamba-2; the same scalar gate form serves Gated DeltaNet), fused
+ * into the append so that no separate elementwise pass writes alpha. Per
+ * record (b, i, h):
+ *     Delta = softplus(dt[b][i][h] + dt_bias[h]),  alpha = exp(-Delta * A[h])
+ * with softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|) in
+ * fp32. The pages give alpha as an input ("How it works": the buffer holds the
+ * records (alpha, k, v)); this form of it is the reading taken for the step on
+ * the path's input side (the thread's question on prefix caching and the
+ * neighbouring layer steps is where the pages leave it open).
+ *   dt [B][T][H]; A [H] (decay rate per head, A >= 0 gives alpha in (0, 1]);
+ *   dt_bias [H] or NULL (zero); k, v, beta as for replayssm_append.
+ * Scalar-gate kinds only: KDA returns REPLAYSSM_ENOTSUP. Everything else
+ * (slots, p += T, overflow flag) is exactly replayssm_append. */
+int replayssm_append_dt(const replayssm_config* cfg, const replayssm_state* st, int T,
+                        const float* dt, const float* A, const float* dt_bias, const float* k,
+                        const float* v, const float* beta, void* stream);
+
 /* One standard decoding step: the single pending record (appended by
  * replayssm_append with T = 1) is the new token t.
  *   - if h + 1 > L, the h committed records are first folded into the

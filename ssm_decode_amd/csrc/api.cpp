@@ -227,17 +227,16 @@ int replayssm_read_error(const replayssm_state* st, int32_t* err_out, void* stre
   return hip_result(e, "read_error");
 }
 
-int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int T,
-                     const float* alpha, const float* k, const float* v, const float* beta,
-                     void* stream) {
-  if (int r = check_config(cfg)) return r;
-  if (int r = check_state(cfg, st)) return r;
-  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
-  NEED(alpha);
+static int append_common(const replayssm_config* cfg, const replayssm_state* st, int T, const float* alpha,
+                         const float* dt, const float* A, const float* dt_bias, const float* k, const float* v,
+                         const float* beta, void* stream) {
   NEED(k);
   NEED(v);
   if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
   rs::AppendArgs a{};
+  a.dt = dt;
+  a.A = A;
+  a.dt_bias = dt_bias;
   a.ring_alpha = st->ring_alpha;
   a.ring_beta = st->ring_beta;
   a.ring_k = st->ring_k;
@@ -261,7 +260,30 @@ int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int
   a.T_max = cfg->T_max;
   // float4 units per sequence: k rows, KDA gate rows, v rows
   a.units_per_seq = T * cfg->H * ((cfg->kind == REPLAYSSM_KDA ? 2 : 1) * cfg->dk + cfg->dv) / 4;
-  return hip_result(rs::launch_append(cfg->kind, a, as_stream(stream)), "append");
+  return hip_result(rs::launch_append(cfg->kind, a, as_stream(stream)), dt ? "append_dt" : "append");
+}
+
+int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int T,
+                     const float* alpha, const float* k, const float* v, const float* beta,
+                     void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
+  NEED(alpha);
+  return append_common(cfg, st, T, alpha, nullptr, nullptr, nullptr, k, v, beta, stream);
+}
+
+int replayssm_append_dt(const replayssm_config* cfg, const replayssm_state* st, int T, const float* dt,
+                        const float* A, const float* dt_bias, const float* k, const float* v, const float* beta,
+                        void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st)) return r;
+  if (cfg->kind == REPLAYSSM_KDA)
+    return fail(REPLAYSSM_ENOTSUP, "append_dt computes a scalar decay per record; KDA gates are per channel");
+  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
+  NEED(dt);
+  NEED(A);
+  return append_common(cfg, st, T, nullptr, dt, A, dt_bias, k, v, beta, stream);
 }
 
 int replayssm_decode(const replayssm_config* cfg, const replayssm_state* st, const float* q,

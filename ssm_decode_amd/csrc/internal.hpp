@@ -86,6 +86,11 @@ struct AppendArgs {
   const float* beta;
   const float* k;
   const float* v;
+  // decay from the raw time step (replayssm_append_dt): alpha is NULL and
+  // alpha = exp(-softplus(dt + dt_bias[h]) * A[h]); dt_bias may be NULL
+  const float* dt;       // [B][T][H]
+  const float* A;        // [H]
+  const float* dt_bias;  // [H] or NULL
   int B, H, dv, dk, C, T, T_max;
   int units_per_seq;  // float4 units of k and v per sequence
 };

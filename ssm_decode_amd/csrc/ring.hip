@@ -44,6 +44,15 @@ hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items
   return hipSuccess;
 }
 
+// A record's decay from its raw time step: Delta = softplus(dt + dt_bias[h]),
+// alpha = exp(-Delta A[h]), softplus in the form max(x, 0) + log1p(e^-|x|),
+// which neither overflows for large x nor loses the small values for x << 0.
+__device__ __forceinline__ float decay_from_dt(const AppendArgs& a, int64_t src, int hd) {
+  const float x = a.dt[src] + (a.dt_bias ? a.dt_bias[hd] : 0.f);
+  const float delta = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+  return expf(-delta * a.A[hd]);
+}
+
 // Append: the T new records of every head of sequence b go to ring slots
 // (head + h + p + i) mod C ("ReplaySSM: Cache SSM Inputs, Not State", How it
 // works: each step appends its inputs; drafts are appended together and the
@@ -96,7 +105,7 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
         const int slot = (first + i) % C;
         const int64_t dst = ((int64_t)b * H + hd) * C + slot;
         const int64_t src = ((int64_t)b * T + i) * H + hd;
-        if (KIND != REPLAYSSM_KDA) a.ring_alpha[dst] = a.alpha[src];
+        if (KIND != REPLAYSSM_KDA) a.ring_alpha[dst] = a.dt ? decay_from_dt(a, src, hd) : a.alpha[src];
         if (KIND != REPLAYSSM_MAMBA2) a.ring_beta[dst] = a.beta[src];
       }
     }

@@ -9,6 +9,8 @@ from .inputs import (  # noqa: F401
     WORKLOADS,
     Workload,
     host_accept,
+    host_decay_params,
+    host_time_steps,
     host_initial_state,
     host_step,
     device_accept,

@@ -36,7 +36,7 @@ from typing import Dict, Optional
 import numpy as np
 
 # field ids of the per-step streams
-_F_ALPHA_DT, _F_ALPHA_A, _F_K, _F_V, _F_Q, _F_BETA, _F_S0, _F_ACC = range(8)
+_F_ALPHA_DT, _F_ALPHA_A, _F_K, _F_V, _F_Q, _F_BETA, _F_S0, _F_ACC, _F_DT_RAW, _F_A_HEAD, _F_DT_BIAS = range(11)
 
 
 @dataclass(frozen=True)
@@ -132,6 +132,19 @@ def host_step(seed: int, wid: int, step: int, shape: LayerShape, T: int,
         out["beta"] = (1.0 / (1.0 + np.exp(-bz))).astype(np.float32)
     out["v"] = _rng(seed, wid, step, _F_V).standard_normal((B, T, H, P)).astype(np.float32)
     return out
+
+
+def host_time_steps(seed: int, wid: int, step: int, shape: LayerShape, T: int) -> np.ndarray:
+    """Raw time-step inputs dt ~ N(0, 1), [B, T, H] float32 (for the decay-from-dt append)."""
+    return _rng(seed, wid, step, _F_DT_RAW).standard_normal((shape.B, T, shape.H)).astype(np.float32)
+
+
+def host_decay_params(seed: int, wid: int, shape: LayerShape):
+    """Per-head decay rate A ~ U(0.5, 2) and time-step bias dt_bias ~ N(0, 0.5^2), each [H] float32
+    (the per-head form of the Mamba-2 recipe's a ~ U(0.5, 2))."""
+    A = _rng(seed, wid, 0, _F_A_HEAD).uniform(0.5, 2.0, shape.H).astype(np.float32)
+    bias = (_rng(seed, wid, 0, _F_DT_BIAS).standard_normal(shape.H) * 0.5).astype(np.float32)
+    return A, bias
 
 
 def host_initial_state(seed: int, wid: int, shape: LayerShape, sigma: float) -> np.ndarray:

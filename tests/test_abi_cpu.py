@@ -111,6 +111,19 @@ def test_calls_reject_bad_arguments_before_enqueueing(rs):
     assert L.replayssm_append(ctypes.byref(cfg), ctypes.byref(st_ok), 0, fake, fake, fake, None, None) == rs.EINVAL
     assert L.replayssm_append(ctypes.byref(cfg), ctypes.byref(st_ok), 5, fake, fake, fake, None, None) == rs.EINVAL
     assert "T=5" in rs.last_error()
+    assert L.replayssm_append_dt(ctypes.byref(cfg), ctypes.byref(st_ok), 0, fake, fake, None, fake, fake, None,
+                                 None) == rs.EINVAL
+    assert L.replayssm_append_dt(ctypes.byref(cfg), ctypes.byref(st_ok), 1, fake, None, None, fake, fake, None,
+                                 None) == rs.EINVAL
+    assert "A is NULL" in rs.last_error()
+    assert L.replayssm_append_dt(ctypes.byref(cfg), ctypes.byref(st_ok), 1, None, fake, None, fake, fake, None,
+                                 None) == rs.EINVAL
+    cfg_k = rs.make_config("kda", "fp32", 2, 3, 64, 128, 16, 4)
+    st_k = rs.State(*([fake] * 13))
+    st_k.lp = None
+    st_k.ring_vraw = None
+    assert L.replayssm_append_dt(ctypes.byref(cfg_k), ctypes.byref(st_k), 1, fake, fake, None, fake, fake, fake,
+                                 None) == rs.ENOTSUP
     assert L.replayssm_verify(ctypes.byref(cfg), ctypes.byref(st_ok), 9, fake, fake, None) == rs.EINVAL
     assert L.replayssm_decode(ctypes.byref(cfg), ctypes.byref(st_ok), fake + 4, fake, None) == rs.EINVAL
     assert "aligned" in rs.last_error()
