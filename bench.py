@@ -1,7 +1,7 @@
 """Benchmark of the ReplaySSM decode path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick] [--sweep]
-                    [--window-sweep]
+                    [--window-sweep] [--flush-only] [--leg NAME]
 
 A step of the headline workload is one standard decoding step of a Mamba-2 SSM
 layer at B=256, H=128, P=64, N=128 (4 MiB fp32 state per sequence), L=16:
@@ -18,7 +18,10 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
              steps) / its average launch duration, both measured live in a second
              pass with events around each launch, against 8 TB/s
   fused      the same step as one replayssm_decode_step launch
+  decode_from_dt  the step with replayssm_append_dt (decay computed from the raw time step)
   eager      the conventional kernel that loads and stores the state every step
+  flush      standalone replayssm_flush launches (16 records folded per head): HBM rate and
+             MFMA rate against the fp32 matrix peak
   workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint;
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
              each warm (one layer) and rotated (rounds cycle over layer instances
@@ -177,8 +180,10 @@ def make_pool(torch, synth, shape, T, n_needed, seed, wid, bytes_per_set):
     return [synth.device_step(seed, wid, 1000 + i, shape, T, "cuda") for i in range(n)]
 
 
-def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True, fused=True, precision=None):
-    """Standard-decoding steps (fused append + decode launches, or append then decode)."""
+def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=True, fused=True, precision=None,
+                        from_dt=False):
+    """Standard-decoding steps (fused append + decode launches, or append then decode). With from_dt
+    the append is replayssm_append_dt (each record's decay computed from its raw time step)."""
     sh = w.shape
     prec = precision or w.precision
     cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, 1)
@@ -186,6 +191,10 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
     layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
     rb = record_bytes(sh.kind, sh.P, sh.N)
     pool = make_pool(torch, synth, sh, 1, steps + warmup, seed, w.wid, sh.B * sh.H * (rb + 4 * (sh.N + sh.P)))
+    if from_dt:
+        A, bias = synth.device_decay_params(seed, w.wid, sh, "cuda")
+        for i, x in enumerate(pool):
+            x["dt"] = synth.device_time_steps(seed, w.wid, 1000 + i, sh, 1, "cuda")
     out = torch.empty((sh.B, sh.H, sh.P), dtype=torch.float32, device="cuda")
     st, stream = layer.struct, torch.cuda.current_stream()
 
@@ -194,7 +203,10 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
         if fused:
             rs.decode_step(cfg, st, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
         else:
-            rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+            if from_dt:
+                rs.append_dt(cfg, st, 1, x["dt"], A, bias, x["k"], x["v"], x.get("beta"), stream)
+            else:
+                rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
             rs.decode(cfg, st, x["q"], out, stream)
 
     for i in range(warmup):
@@ -226,7 +238,10 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
                 rs.decode_step(cfg, st, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], out, stream)
                 evs[i][1].record(stream)
             else:
-                rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
+                if from_dt:
+                    rs.append_dt(cfg, st, 1, x["dt"], A, bias, x["k"], x["v"], x.get("beta"), stream)
+                else:
+                    rs.append(cfg, st, 1, x["alpha"], x["k"], x["v"], x.get("beta"), stream)
                 evs[i][0].record(stream)
                 rs.decode(cfg, st, x["q"], out, stream)
                 evs[i][1].record(stream)
@@ -572,6 +587,8 @@ def cpu_baseline(synth, w, seed, seconds, threads=None, seqs=64):
 LEGS = {
     "mamba2_decode": lambda torch, rs, synth, k, w, seed: run_standard_decode(
         torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=False),
+    "mamba2_decode_dt": lambda torch, rs, synth, k, w, seed: run_standard_decode(
+        torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=False, from_dt=True),
     "mamba2_decode_fused": lambda torch, rs, synth, k, w, seed: run_standard_decode(
         torch, rs, synth, synth.WORKLOADS["mamba2_decode_b256"], k, w, seed, fused=True),
     "mamba2_spec": lambda torch, rs, synth, k, w, seed: run_spec(
@@ -666,6 +683,13 @@ def main():
                                  "kernel_avg_us": tp["kernel_avg_us"], "plain_step_us": tp["plain_avg_us"],
                                  "fold_step_us": tp["fold_avg_us"],
                                  "step": "replayssm_append then replayssm_decode, bf16 copy read off-fold"}
+    if not args.quick:
+        dtl = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False,
+                                  kernel_pass=False, from_dt=True)
+        line["decode_from_dt"] = {"tokens_per_s": dtl["tokens"] / (dtl["ms"] * 1e-3),
+                                  "ms_per_step": dtl["ms"] / dtl["steps"],
+                                  "headline_ms_per_step": main_res["ms"] / args.steps,
+                                  "step": "replayssm_append_dt (decay from the raw time step) then replayssm_decode"}
     if not args.quick:
         eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
         line["eager"] = {"tokens_per_s": eg["tokens"] / (eg["ms"] * 1e-3), "gbs": eg["gbs"],

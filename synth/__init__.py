@@ -14,6 +14,8 @@ from .inputs import (  # noqa: F401
     host_initial_state,
     host_step,
     device_accept,
+    device_decay_params,
+    device_time_steps,
     device_initial_state,
     device_step,
 )

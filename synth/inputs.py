@@ -217,6 +217,25 @@ def device_step(seed: int, wid: int, step: int, shape: LayerShape, T: int, devic
     return out
 
 
+def device_time_steps(seed: int, wid: int, step: int, shape: LayerShape, T: int, device):
+    """As host_time_steps, drawn on `device`."""
+    import torch
+
+    return torch.randn((shape.B, T, shape.H), dtype=torch.float32, device=device,
+                       generator=_gen(device, seed, wid, step, _F_DT_RAW))
+
+
+def device_decay_params(seed: int, wid: int, shape: LayerShape, device):
+    """As host_decay_params, drawn on `device`."""
+    import torch
+
+    A = torch.empty(shape.H, dtype=torch.float32, device=device).uniform_(
+        0.5, 2.0, generator=_gen(device, seed, wid, 0, _F_A_HEAD))
+    bias = torch.empty(shape.H, dtype=torch.float32, device=device).normal_(
+        0.0, 0.5, generator=_gen(device, seed, wid, 0, _F_DT_BIAS))
+    return A, bias
+
+
 def device_initial_state(seed: int, wid: int, shape: LayerShape, sigma: float, device):
     import torch
 
