@@ -303,8 +303,13 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
                                             f32x4 (&S)[NT], RecRegs<TMAX>& rr, const Item nit, const SeqPtr nptr,
                                             const Route nrt) {
   constexpr int DK = NT * 16;
-  constexpr int LPR = DK / 4;       // lanes per k row in the dot phase (float4 each)
-  constexpr int RPI = kWave / LPR;  // k rows per wavefront pass
+  // Dot phase: each lane takes CPL float4 chunks of a k row (chunks li and
+  // li + LPR), so LPR lanes share a row and a wavefront pass covers RPI rows.
+  // Two chunks per lane halve the passes and the reduction tree loses a level;
+  // the verify kernels with 8 drafts keep one chunk (their registers are full).
+  constexpr int CPL = (KIND != REPLAYSSM_KDA && TMAX <= 4 && DK >= 32) ? 2 : 1;
+  constexpr int LPR = DK / (4 * CPL);
+  constexpr int RPI = kWave / LPR;
   constexpr bool GDN = kind_gdn(KIND);
   constexpr bool KDA = KIND == REPLAYSSM_KDA;
 
@@ -461,34 +466,61 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     // one draft at a time, q_i (and k_i) re-read from LDS per pass: a register
     // copy of every draft's vectors would cost 4 (GDN: 8) registers per draft
     const int sub = lane / LPR, li = lane % LPR;
-    for (int base = r0 + wave * RPI; base < R; base += W * RPI) {
-      const int r = base + sub;
-      const bool valid = r < R;
-      f32x4 kr = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (valid) kr = ld4(sm + lds.k + r * lds.dks + 4 * li);
-      f32x4 dec = {1.f, 1.f, 1.f, 1.f};  // KDA: gates of records (r, hc + i] for a draft row r
+    if constexpr (CPL == 1) {
+      for (int base = r0 + wave * RPI; base < R; base += W * RPI) {
+        const int r = base + sub;
+        const bool valid = r < R;
+        f32x4 kr = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (valid) kr = ld4(sm + lds.k + r * lds.dks + 4 * li);
+        f32x4 dec = {1.f, 1.f, 1.f, 1.f};  // KDA: gates of records (r, hc + i] for a draft row r
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i) {
-        if (i < T) {
-          f32x4 kx = kr;
-          const float* qrow = sm + lds.q + i * DK + 4 * li;
-          const float* krow = sm + lds.k + (hc + i) * lds.dks + 4 * li;
-          if constexpr (KDA) {
-            if (r < hc) {
-              // a committed row (already carried to the last committed record)
-              // meets the drafts' gated vectors
-              qrow = sm + lds.qg + i * DK + 4 * li;
-              krow = sm + lds.kg + i * DK + 4 * li;
-            } else {
-              if (i > r - hc) dec *= ld4(sm + lds.alpha + (hc + i) * lds.dks + 4 * li);
-              kx = kr * dec;
+        for (int i = 0; i < TMAX; ++i) {
+          if (i < T) {
+            f32x4 kx = kr;
+            const float* qrow = sm + lds.q + i * DK + 4 * li;
+            const float* krow = sm + lds.k + (hc + i) * lds.dks + 4 * li;
+            if constexpr (KDA) {
+              if (r < hc) {
+                // a committed row (already carried to the last committed record)
+                // meets the drafts' gated vectors
+                qrow = sm + lds.qg + i * DK + 4 * li;
+                krow = sm + lds.kg + i * DK + 4 * li;
+              } else {
+                if (i > r - hc) dec *= ld4(sm + lds.alpha + (hc + i) * lds.dks + 4 * li);
+                kx = kr * dec;
+              }
+            }
+            const float dq = sum_width<LPR>(dot4(kx, ld4(qrow)));
+            if (valid && li == 0) sm[lds.cq + r * TMAX + i] = dq;
+            if constexpr (GDN) {
+              const float dkk = sum_width<LPR>(dot4(kx, ld4(krow)));
+              if (valid && li == 0) sm[lds.ck + r * TMAX + i] = dkk;
             }
           }
-          const float dq = sum_width<LPR>(dot4(kx, ld4(qrow)));
-          if (valid && li == 0) sm[lds.cq + r * TMAX + i] = dq;
-          if constexpr (GDN) {
-            const float dkk = sum_width<LPR>(dot4(kx, ld4(krow)));
-            if (valid && li == 0) sm[lds.ck + r * TMAX + i] = dkk;
+        }
+      }
+    } else {
+      // two chunks per lane (Mamba-2 and GDN): chunks li and li + LPR of the row
+      for (int base = r0 + wave * RPI; base < R; base += W * RPI) {
+        const int r = base + sub;
+        const bool valid = r < R;
+        const int o0 = 4 * li, o1 = 4 * (li + LPR);
+        f32x4 k0 = f32x4{0.f, 0.f, 0.f, 0.f}, k1 = k0;
+        if (valid) {
+          k0 = ld4(sm + lds.k + r * lds.dks + o0);
+          k1 = ld4(sm + lds.k + r * lds.dks + o1);
+        }
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          if (i < T) {
+            const float* qrow = sm + lds.q + i * DK;
+            const float dq = sum_width<LPR>(fma4(k1, ld4(qrow + o1), dot4(k0, ld4(qrow + o0))));
+            if (valid && li == 0) sm[lds.cq + r * TMAX + i] = dq;
+            if constexpr (GDN) {
+              const float* krow = sm + lds.k + (hc + i) * lds.dks;
+              const float dkk = sum_width<LPR>(fma4(k1, ld4(krow + o1), dot4(k0, ld4(krow + o0))));
+              if (valid && li == 0) sm[lds.ck + r * TMAX + i] = dkk;
+            }
           }
         }
       }
