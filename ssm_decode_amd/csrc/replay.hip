@@ -433,11 +433,14 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   if (!KDA && outputs) {
     const bool wide = R - r0 + 1 > kWave;
     if (!wide) {
-      for (int job = wave; job < 2 * T; job += W) {
-        const int i = job >> 1;
+      // (Mamba-2 outputs read only gq: its drafts need no state before them)
+      constexpr int kJobsPerDraft = GDN ? 2 : 1;
+      for (int job = wave; job < kJobsPerDraft * T; job += W) {
+        const int i = GDN ? job >> 1 : job;
+        const bool kjob = GDN && (job & 1);
         const int first = r0 - 1, last = R - 1;
-        const int e = (job & 1) ? hc + i - 1 : hc + i;
-        float* out = sm + ((job & 1) ? lds.gk : lds.gq) + i;
+        const int e = kjob ? hc + i - 1 : hc + i;
+        float* out = sm + (kjob ? lds.gk : lds.gq) + i;
         const int r = first + lane;
         const float x = suffix_product64((r + 1 <= e) ? sm[lds.alpha + r + 1] : 1.f, lane);
         if (r <= last) out[(r + 1) * TMAX] = (r <= e) ? x : 0.f;
