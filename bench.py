@@ -22,7 +22,8 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
   eager      the conventional kernel that loads and stores the state every step
   flush      standalone replayssm_flush launches (16 records folded per head): HBM rate and
              MFMA rate against the fp32 matrix peak
-  workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint;
+  workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint (with its
+             small-batch rounds, B in {1, 32}, launched eagerly and replayed from a HIP graph);
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
              each warm (one layer) and rotated (rounds cycle over layer instances
              holding >= 2 GiB of state, so the on-package cache cannot hold it)
@@ -420,6 +421,51 @@ def run_flush(torch, rs, synth, w, cycles, warmup, seed, precision=None):
             "mfma_frac": flops / (us * 1e6) / MFMA_F32_PEAK_TFLOPS, "precision": prec}
 
 
+def run_spec_graph(torch, rs, synth, w, B, K, reps, seed, precision=None):
+    """Small-batch speculative rounds, eager against HIP-graph replay: K rounds (fused append +
+    verify, then accept) captured once with torch.cuda.CUDAGraph around the library's calls and
+    replayed `reps` times, against the same K rounds launched eagerly `reps` times."""
+    sh = synth.LayerShape(w.shape.kind, B, w.shape.H, w.shape.P, w.shape.N)
+    prec = precision or w.precision
+    T = w.T if w.T > 1 else int(w.extra.get("spec_T", 4))
+    cfg = rs.make_config(sh.kind, prec, sh.B, sh.H, sh.P, sh.N, w.L, T)
+    layer = rs.LayerState(cfg)
+    layer.import_state(synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda"))
+    xs = [synth.device_step(seed, w.wid, 3000 + r, sh, T, "cuda") for r in range(K)]
+    accs = [synth.device_accept(seed, w.wid, 3000 + r, sh.B, T, "cuda") for r in range(K)]
+    outs = [torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda") for _ in range(K)]
+    accepted = int(sum(int(a.sum().item()) for a in accs))
+
+    def rounds():
+        for r in range(K):
+            x = xs[r]
+            rs.verify_step(cfg, layer.struct, T, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], outs[r])
+            rs.accept(cfg, layer.struct, accs[r])
+
+    for _ in range(2):
+        rounds()
+    with Timer(torch) as te:
+        for _ in range(reps):
+            rounds()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        rounds()
+    graph.replay()
+    with Timer(torch) as tg:
+        for _ in range(reps):
+            graph.replay()
+    err = rs.read_error(layer.struct)
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    n = reps * K
+    return {"B": B, "T": T, "precision": prec, "rounds_per_graph": K,
+            "eager_us_per_round": te.ms * 1e3 / n, "graph_us_per_round": tg.ms * 1e3 / n,
+            "eager_accepted_tokens_per_s": reps * accepted / (te.ms * 1e-3),
+            "graph_accepted_tokens_per_s": reps * accepted / (tg.ms * 1e-3)}
+
+
 def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
     sh = w.shape
     cfg = rs.make_config(sh.kind, "fp32", sh.B, sh.H, sh.P, sh.N, w.L, T)
@@ -743,6 +789,8 @@ def main():
             r = run_spec(torch, rs, synth, w4, 128, 8, args.seed, precision=prec)
             r4[prec] = {"accepted_tokens_per_s": r["accepted_tokens"] / (r["ms"] * 1e-3),
                         "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"]}
+        r4["small_batch_graph"] = {f"B{B}": run_spec_graph(torch, rs, synth, w4, B, 16, 20, args.seed)
+                                   for B in (1, 32)}
         if args.sweep:
             sweep = {}
             for B in (1, 32, 256, 512):
