@@ -328,6 +328,58 @@ int replayssm_eager_verify(const replayssm_config* cfg, float* pool, const int32
 int replayssm_eager_accept(const replayssm_config* cfg, int32_t* slot, const int32_t* accepted,
                            int T, void* stream);
 
+/* ---- the convolution on the input side, kept as an input ring ------------
+ * Mamba-2 passes the input projection's D channels (x, and the B and C that
+ * become k and q) through a short causal depthwise convolution of width W with
+ * a bias and SiLU before the state-space step:
+ *     y_t[c] = act(bias[c] + sum_{j<W} w[c][j] x_{t-W+1+j}[c]),  x_s = 0 for s < 0.
+ * The pages leave this neighbouring step open; taken the ReplaySSM way ("How it
+ * works": cache the inputs, not the state; Speculative decoding: acceptance
+ * moves a pointer), its state is its last W - 1 inputs, kept in a ring of
+ * capacity Cc = W - 1 + T_max per sequence. A step appends T inputs after the
+ * window and computes each one's output from the window that ends at it;
+ * accepting a drafts moves the window's start by a; rejected inputs are
+ * overwritten by the next step.
+ *   W 1..4, D a multiple of 4, 1 <= T_max <= 8, B 1..65535.
+ * State (caller-owned device memory, 16-byte aligned):
+ *   ring  float [B][Cc][D] (row-major, callers may read it); start, pend, arrive
+ *   int32 [B] (window start slot, pending inputs, library scratch); err int32 [1]. */
+typedef struct replayssm_conv_config {
+  int32_t B;
+  int32_t D;
+  int32_t W;
+  int32_t T_max;
+} replayssm_conv_config;
+
+typedef struct replayssm_conv_state {
+  float* ring;
+  int32_t* start;
+  int32_t* pend;
+  int32_t* arrive;
+  int32_t* err;
+} replayssm_conv_state;
+
+/* Validates cfg; ring bytes (B * Cc * D * 4) and bytes of each int32 [B] array. Host only. */
+int replayssm_conv_sizes(const replayssm_conv_config* cfg, int64_t* ring_bytes, int64_t* ptr_bytes);
+
+/* Zero window (x_s = 0 before the first token), start = pend = 0, err = 0. */
+int replayssm_conv_init(const replayssm_conv_config* cfg, const replayssm_conv_state* st, void* stream);
+
+/* Appends T inputs x [B][T][D] per sequence and writes y [B][T][D]: output i
+ * from the window ending at input i. w [D][W] (PyTorch's conv1d weight
+ * [D][1][W] squeezed), bias [D] or NULL, silu nonzero applies SiLU. With commit
+ * nonzero the T inputs join the window at once (standard decoding); otherwise
+ * they stay pending until replayssm_conv_accept. A sequence with pending inputs
+ * is skipped and flagged (REPLAYSSM_DEVERR_PENDING). */
+int replayssm_conv_step(const replayssm_conv_config* cfg, const replayssm_conv_state* st, int T,
+                        const float* x, const float* w, const float* bias, int silu, int commit,
+                        float* y, void* stream);
+
+/* accepted [B] int32 device array: the first a_b pending inputs join the window;
+ * a outside 0..pend is clamped and flagged (REPLAYSSM_DEVERR_ACCEPT); pend = 0. */
+int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv_state* st,
+                          const int32_t* accepted, void* stream);
+
 /* ---- Measurement helper (not a step of the method) -------------------------------------
  * Reads `bytes` bytes at device address `src` once, in the access pattern of the replay
  * kernel's checkpoint stream (persistent workgroups, 32 KiB per workgroup per pass, 16-byte

@@ -52,6 +52,14 @@ class Sizes(ctypes.Structure):
                 ("err_bytes", _i64), ("ring_vraw_bytes", _i64)]
 
 
+class ConvConfig(ctypes.Structure):
+    _fields_ = [("B", _i32), ("D", _i32), ("W", _i32), ("T_max", _i32)]
+
+
+class ConvState(ctypes.Structure):
+    _fields_ = [("ring", _vp), ("start", _vp), ("pend", _vp), ("arrive", _vp), ("err", _vp)]
+
+
 class ReplaySSMError(RuntimeError):
     def __init__(self, status: int, where: str, text: str):
         super().__init__(f"{where}: status {status} ({text})")
@@ -69,6 +77,11 @@ SIGNATURES = {
     "replayssm_append_dt": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp],
     "replayssm_decode": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp, _vp],
+    "replayssm_conv_sizes": [ctypes.POINTER(ConvConfig), ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
+    "replayssm_conv_init": [ctypes.POINTER(ConvConfig), ctypes.POINTER(ConvState), _vp],
+    "replayssm_conv_step": [ctypes.POINTER(ConvConfig), ctypes.POINTER(ConvState), ctypes.c_int, _vp, _vp, _vp,
+                            ctypes.c_int, ctypes.c_int, _vp, _vp],
+    "replayssm_conv_accept": [ctypes.POINTER(ConvConfig), ctypes.POINTER(ConvState), _vp, _vp],
     "replayssm_verify": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
     "replayssm_decode_step": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "replayssm_verify_step": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
@@ -304,3 +317,46 @@ class LayerState:
     def pointers(self):
         return {"head": self.head.tolist(), "h": self.h.tolist(), "p": self.p.tolist(),
                 "folded": self.folded.tolist()}
+
+
+# ---- convolution input ring -------------------------------------------------
+
+def make_conv_config(B, D, W=4, T_max=1) -> ConvConfig:
+    return ConvConfig(int(B), int(D), int(W), int(T_max))
+
+
+def conv_sizes(cfg: ConvConfig):
+    ring, ptr = _i64(0), _i64(0)
+    _check(lib().replayssm_conv_sizes(ctypes.byref(cfg), ctypes.byref(ring), ctypes.byref(ptr)), "conv_sizes")
+    return int(ring.value), int(ptr.value)
+
+
+def conv_init(cfg, st, stream=None):
+    _check(lib().replayssm_conv_init(ctypes.byref(cfg), ctypes.byref(st), _s(stream)), "conv_init")
+
+
+def conv_step(cfg, st, T, x, w, bias, silu, commit, y, stream=None):
+    _check(lib().replayssm_conv_step(ctypes.byref(cfg), ctypes.byref(st), int(T), _f32(x), _f32(w), _f32(bias),
+                                     int(bool(silu)), int(bool(commit)), _f32(y), _s(stream)), "conv_step")
+
+
+def conv_accept(cfg, st, accepted, stream=None):
+    _check(lib().replayssm_conv_accept(ctypes.byref(cfg), ctypes.byref(st), _i32t(accepted), _s(stream)),
+           "conv_accept")
+
+
+class ConvLayer:
+    """Device memory (torch tensors) for one layer's convolution input ring, plus the C struct;
+    replayssm_conv_init is called once on construction."""
+
+    def __init__(self, cfg: ConvConfig, device="cuda", stream=None):
+        self.cfg = cfg
+        conv_sizes(cfg)  # validates
+        self.Cc = cfg.W - 1 + cfg.T_max
+        self.ring = torch.empty((cfg.B, self.Cc, cfg.D), dtype=torch.float32, device=device)
+        self.start = torch.empty(cfg.B, dtype=torch.int32, device=device)
+        self.pend = torch.empty(cfg.B, dtype=torch.int32, device=device)
+        self.arrive = torch.empty(cfg.B, dtype=torch.int32, device=device)
+        self.err = torch.empty(4, dtype=torch.int32, device=device)
+        self.struct = ConvState(*[t.data_ptr() for t in (self.ring, self.start, self.pend, self.arrive, self.err)])
+        conv_init(cfg, self.struct, stream)

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libreplayssm.so")
-SOURCES = ["replay.hip", "ring.hip", "eager.hip", "probe.hip", "api.cpp"]
+SOURCES = ["replay.hip", "ring.hip", "eager.hip", "probe.hip", "conv.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "conv.hpp"
 #include "internal.hpp"
 #include "replayssm.h"
 
@@ -475,6 +476,92 @@ int replayssm_probe_read(const void* src, int64_t bytes, float* sink, void* stre
   if (bytes <= 0 || bytes % 16 != 0)
     return fail(REPLAYSSM_EINVAL, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
   return hip_result(rs::launch_probe_read(src, bytes, sink, as_stream(stream)), "probe_read");
+}
+
+}  // extern "C"
+
+// ---- convolution input ring ----------------------------------------------
+
+namespace {
+
+int check_conv(const replayssm_conv_config* c) {
+  if (c == nullptr) return fail(REPLAYSSM_EINVAL, "cfg is NULL");
+  if (c->B < 1 || c->B > 65535) return fail(REPLAYSSM_EINVAL, "B=%d outside 1..65535", c->B);
+  if (c->D < 4 || c->D % 4 != 0) return fail(REPLAYSSM_EINVAL, "D=%d must be a positive multiple of 4", c->D);
+  if ((int64_t)c->D / 4 > (int64_t)256 * 65535) return fail(REPLAYSSM_EINVAL, "D=%d too large", c->D);
+  if (c->W < 1 || c->W > rs::kConvMaxW) return fail(REPLAYSSM_EINVAL, "W=%d outside 1..%d", c->W, rs::kConvMaxW);
+  if (c->T_max < 1 || c->T_max > rs::kMaxDrafts) return fail(REPLAYSSM_EINVAL, "T_max=%d outside 1..8", c->T_max);
+  return REPLAYSSM_OK;
+}
+
+int check_conv_state(const replayssm_conv_state* s) {
+  if (s == nullptr) return fail(REPLAYSSM_EINVAL, "state is NULL");
+  NEED(s->ring);
+  NEED(s->start);
+  NEED(s->pend);
+  NEED(s->arrive);
+  NEED(s->err);
+  return REPLAYSSM_OK;
+}
+
+rs::ConvArgs conv_args(const replayssm_conv_config* c, const replayssm_conv_state* s) {
+  rs::ConvArgs a{};
+  a.ring = s->ring;
+  a.start = s->start;
+  a.pend = s->pend;
+  a.arrive = s->arrive;
+  a.err = s->err;
+  a.B = c->B;
+  a.D = c->D;
+  a.W = c->W;
+  a.T_max = c->T_max;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int replayssm_conv_sizes(const replayssm_conv_config* cfg, int64_t* ring_bytes, int64_t* ptr_bytes) {
+  if (int r = check_conv(cfg)) return r;
+  if (ring_bytes) *ring_bytes = (int64_t)cfg->B * (cfg->W - 1 + cfg->T_max) * cfg->D * 4;
+  if (ptr_bytes) *ptr_bytes = (int64_t)cfg->B * 4;
+  return REPLAYSSM_OK;
+}
+
+int replayssm_conv_init(const replayssm_conv_config* cfg, const replayssm_conv_state* st, void* stream) {
+  if (int r = check_conv(cfg)) return r;
+  if (int r = check_conv_state(st)) return r;
+  return hip_result(rs::launch_conv_init(conv_args(cfg, st), as_stream(stream)), "conv_init");
+}
+
+int replayssm_conv_step(const replayssm_conv_config* cfg, const replayssm_conv_state* st, int T,
+                        const float* x, const float* w, const float* bias, int silu, int commit,
+                        float* y, void* stream) {
+  if (int r = check_conv(cfg)) return r;
+  if (int r = check_conv_state(st)) return r;
+  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
+  NEED(x);
+  NEED(w);
+  NEED(y);
+  if (bias && !aligned(bias)) return fail(REPLAYSSM_EINVAL, "bias is not 16-byte aligned");
+  rs::ConvArgs a = conv_args(cfg, st);
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.y = y;
+  a.T = T;
+  a.silu = silu ? 1 : 0;
+  a.commit = commit ? 1 : 0;
+  return hip_result(rs::launch_conv_step(a, as_stream(stream)), "conv_step");
+}
+
+int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv_state* st,
+                          const int32_t* accepted, void* stream) {
+  if (int r = check_conv(cfg)) return r;
+  if (int r = check_conv_state(st)) return r;
+  NEED(accepted);
+  return hip_result(rs::launch_conv_accept(conv_args(cfg, st), accepted, as_stream(stream)), "conv_accept");
 }
 
 }  // extern "C"

@@ -9,11 +9,14 @@ from .inputs import (  # noqa: F401
     WORKLOADS,
     Workload,
     host_accept,
+    host_conv_inputs,
+    host_conv_params,
     host_decay_params,
     host_time_steps,
     host_initial_state,
     host_step,
     device_accept,
+    device_conv_inputs,
     device_decay_params,
     device_time_steps,
     device_initial_state,

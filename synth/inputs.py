@@ -36,7 +36,8 @@ from typing import Dict, Optional
 import numpy as np
 
 # field ids of the per-step streams
-_F_ALPHA_DT, _F_ALPHA_A, _F_K, _F_V, _F_Q, _F_BETA, _F_S0, _F_ACC, _F_DT_RAW, _F_A_HEAD, _F_DT_BIAS = range(11)
+_F_ALPHA_DT, _F_ALPHA_A, _F_K, _F_V, _F_Q, _F_BETA, _F_S0, _F_ACC, _F_DT_RAW, _F_A_HEAD, _F_DT_BIAS, \
+    _F_CONV_X, _F_CONV_W, _F_CONV_B = range(14)
 
 
 @dataclass(frozen=True)
@@ -147,6 +148,18 @@ def host_decay_params(seed: int, wid: int, shape: LayerShape):
     return A, bias
 
 
+def host_conv_inputs(seed: int, wid: int, step: int, B: int, T: int, D: int) -> np.ndarray:
+    """Input-projection channels entering the short convolution: x ~ N(0, 1), [B, T, D] float32."""
+    return _rng(seed, wid, step, _F_CONV_X).standard_normal((B, T, D)).astype(np.float32)
+
+
+def host_conv_params(seed: int, wid: int, D: int, W: int):
+    """Convolution weights w ~ N(0, 1/W) [D, W] and bias ~ N(0, 0.1^2) [D], float32."""
+    w = (_rng(seed, wid, 0, _F_CONV_W).standard_normal((D, W)) / np.sqrt(W)).astype(np.float32)
+    b = (_rng(seed, wid, 0, _F_CONV_B).standard_normal(D) * 0.1).astype(np.float32)
+    return w, b
+
+
 def host_initial_state(seed: int, wid: int, shape: LayerShape, sigma: float) -> np.ndarray:
     """Initial checkpoint in the logical [B, H, P, N] layout."""
     if sigma == 0.0:
@@ -234,6 +247,13 @@ def device_decay_params(seed: int, wid: int, shape: LayerShape, device):
     bias = torch.empty(shape.H, dtype=torch.float32, device=device).normal_(
         0.0, 0.5, generator=_gen(device, seed, wid, 0, _F_DT_BIAS))
     return A, bias
+
+
+def device_conv_inputs(seed: int, wid: int, step: int, B: int, T: int, D: int, device):
+    """As host_conv_inputs, drawn on `device`."""
+    import torch
+
+    return torch.randn((B, T, D), dtype=torch.float32, device=device, generator=_gen(device, seed, wid, step, _F_CONV_X))
 
 
 def device_initial_state(seed: int, wid: int, shape: LayerShape, sigma: float, device):

@@ -149,6 +149,38 @@ def test_calls_reject_bad_arguments_before_enqueueing(rs):
     assert L.replayssm_probe_read(fake, 1024, None, None) == rs.EINVAL
 
 
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True), (dict(W=1), True), (dict(W=0), False), (dict(W=5), False), (dict(D=6), False),
+    (dict(D=0), False), (dict(T_max=0), False), (dict(T_max=9), False), (dict(B=0), False), (dict(B=70000), False),
+])
+def test_conv_config_validation(rs, kw, ok):
+    base = dict(B=2, D=64, W=4, T_max=4)
+    base.update(kw)
+    cfg = rs.make_conv_config(**base)
+    ring, ptr = ctypes.c_int64(0), ctypes.c_int64(0)
+    code = rs.lib().replayssm_conv_sizes(ctypes.byref(cfg), ctypes.byref(ring), ctypes.byref(ptr))
+    assert (code == rs.OK) == ok
+    if ok:
+        assert ring.value == base["B"] * (base["W"] - 1 + base["T_max"]) * base["D"] * 4 and ptr.value == base["B"] * 4
+
+
+def test_conv_calls_reject_bad_arguments_before_enqueueing(rs):
+    L = rs.lib()
+    cfg = rs.make_conv_config(2, 64, 4, 4)
+    fake = 1 << 20
+    st = rs.ConvState(fake, fake, fake, fake, fake)
+    assert L.replayssm_conv_init(ctypes.byref(cfg), None, None) == rs.EINVAL
+    assert L.replayssm_conv_step(ctypes.byref(cfg), ctypes.byref(st), 0, fake, fake, None, 1, 0, fake, None) == rs.EINVAL
+    assert L.replayssm_conv_step(ctypes.byref(cfg), ctypes.byref(st), 5, fake, fake, None, 1, 0, fake, None) == rs.EINVAL
+    assert L.replayssm_conv_step(ctypes.byref(cfg), ctypes.byref(st), 1, fake, None, None, 1, 0, fake, None) == rs.EINVAL
+    assert L.replayssm_conv_step(ctypes.byref(cfg), ctypes.byref(st), 1, fake, fake, fake + 4, 1, 0, fake,
+                                 None) == rs.EINVAL
+    assert "bias" in rs.last_error()
+    assert L.replayssm_conv_accept(ctypes.byref(cfg), ctypes.byref(st), None, None) == rs.EINVAL
+    bad = rs.ConvState(fake, None, fake, fake, fake)
+    assert L.replayssm_conv_init(ctypes.byref(cfg), ctypes.byref(bad), None) == rs.EINVAL
+
+
 def test_status_strings(rs):
     assert rs.status_string(0) == "ok"
     assert rs.status_string(-1) == "invalid argument"
