@@ -22,6 +22,8 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
   eager      the conventional kernel that loads and stores the state every step
   flush      standalone replayssm_flush launches (16 records folded per head): HBM rate and
              MFMA rate against the fp32 matrix peak
+  conv_input_ring  the input-side short convolution kept as an input ring (replayssm_conv_step)
+             at the layer's 40,960 channels, width 4: standard steps and T=4 rounds
   workloads  speculative verify (T=4), Gated DeltaNet, two-precision checkpoint (with its
              small-batch rounds, B in {1, 32}, launched eagerly and replayed from a HIP graph);
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
@@ -466,6 +468,43 @@ def run_spec_graph(torch, rs, synth, w, B, K, reps, seed, precision=None):
             "graph_accepted_tokens_per_s": reps * accepted / (tg.ms * 1e-3)}
 
 
+def conv_launch_bytes(D, W, T):
+    """Bytes one sequence moves in a conv step: the W - 1 window inputs read, the T inputs read and
+    written to the ring, the T outputs written (weights and bias, shared by all sequences, aside)."""
+    return 4 * D * ((W - 1) + 3 * T)
+
+
+def run_conv(torch, rs, synth, B, D, W, T, steps, warmup, seed, wid=20):
+    """The input-side convolution ring at a Mamba-2 layer's channel count: T = 1 steps commit
+    their input at once; T > 1 rounds leave the drafts pending and accept a prefix ~ U{0..T}.
+    Events around every step launch give the kernel's time."""
+    cfg = rs.make_conv_config(B, D, W, T)
+    layer = rs.ConvLayer(cfg)
+    wh, bh = synth.host_conv_params(seed, wid, D, W)
+    w, b = torch.from_numpy(wh).cuda(), torch.from_numpy(bh).cuda()
+    n = int(max(2, min(8, (1 << 30) // (B * T * D * 4))))
+    xs = [synth.device_conv_inputs(seed, wid, i, B, T, D, "cuda") for i in range(n)]
+    accs = [synth.device_accept(seed, wid, i, B, T, "cuda") for i in range(n)]
+    y = torch.empty((B, T, D), dtype=torch.float32, device="cuda")
+    st, stream = layer.struct, torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(warmup + steps):
+        if i >= warmup:
+            evs[i - warmup][0].record(stream)
+        rs.conv_step(cfg, st, T, xs[i % n], w, b, True, T == 1, y, stream)
+        if i >= warmup:
+            evs[i - warmup][1].record(stream)
+        if T > 1:
+            rs.conv_accept(cfg, st, accs[i % n], stream)
+    torch.cuda.synchronize()
+    if int(layer.err[0].item()):
+        raise RuntimeError(f"conv error word {int(layer.err[0].item())}")
+    us = float(np.mean([a.elapsed_time(e) for a, e in evs]) * 1e3)
+    nbytes = conv_launch_bytes(D, W, T) * B
+    return {"B": B, "D": D, "W": W, "T": T, "step_us": us, "bytes_per_launch": nbytes, "gbs": nbytes / (us * 1e3),
+            "hbm_frac": nbytes / (us * 1e3) / HBM_PEAK_GBS}
+
+
 def run_eager(torch, rs, synth, w, steps, warmup, seed, T=1):
     sh = w.shape
     cfg = rs.make_config(sh.kind, "fp32", sh.B, sh.H, sh.P, sh.N, w.L, T)
@@ -654,6 +693,7 @@ LEGS = {
         torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], k, w, seed, precision="fp32_hp_bf16_lp"),
     "kda_decode": lambda torch, rs, synth, k, w, seed: run_standard_decode(
         torch, rs, synth, synth.WORKLOADS["kda_decode_b256"], k, w, seed, fused=False),
+    "conv_decode": lambda torch, rs, synth, k, w, seed: run_conv(torch, rs, synth, 256, 40960, 4, 1, k, w, seed),
     "kda_spec": lambda torch, rs, synth, k, w, seed: run_spec(
         torch, rs, synth, synth.WORKLOADS["kda_decode_b256"], k, w, seed),
 }
@@ -783,6 +823,9 @@ def main():
               "gdn_fp32_hp_bf16_lp": run_flush(torch, rs, synth, synth.WORKLOADS["gdn_decode_b256"], 16, 2,
                                                args.seed, precision="fp32_hp_bf16_lp")}
         line["flush"] = fl
+        # the input side of the Mamba-2 layer: x (8192) and B, C (2 x 128 x 128) channels, width 4
+        line["conv_input_ring"] = {f"T{T}": run_conv(torch, rs, synth, 256, 40960, 4, T, 64, 8, args.seed)
+                                   for T in (1, 4)}
         w4 = synth.WORKLOADS["mamba2_2prec_b256"]
         r4 = {}
         for prec in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):

@@ -69,3 +69,9 @@ def test_state_byte_ratio_against_eager():
     # checkpoint read every step plus one write per 16-token window, against a load and a store per token
     replay_state = 4 * P * N * (1 + 1 / 16)
     assert round(2 * 4 * P * N / replay_state, 2) == 1.88
+
+
+def test_conv_ring_bytes():
+    # window of W - 1 inputs read, T inputs read and written to the ring, T outputs written
+    assert bench.conv_launch_bytes(40960, 4, 1) == 4 * 40960 * 6
+    assert bench.conv_launch_bytes(40960, 4, 4) == 4 * 40960 * 15
