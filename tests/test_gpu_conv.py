@@ -118,3 +118,14 @@ def test_contract_violations_are_flagged_and_skipped():
     assert int(r.layer.err[0].item()) & rs.DEVERR_ACCEPT
     np.testing.assert_array_equal(r.layer.start.cpu().numpy(), [2, 1])
     np.testing.assert_array_equal(r.layer.pend.cpu().numpy(), [0, 0])
+
+
+def test_committing_several_inputs_at_once():
+    """commit with T > 1 (several tokens in one call, e.g. a prompt's tail), mixed with rounds."""
+    r = ConvRun(3, 96, 4, 4, wid=99)
+    for rnd in range(8):
+        r.step(4 if rnd % 2 == 0 else 3, commit=True)
+        r.step(4, commit=False)
+        r.accept(host_accept(0, 99, rnd, 3, 4))
+    assert r.max_rel <= TOL, r.max_rel
+    assert int(r.layer.err[0].item()) == 0
