@@ -86,25 +86,27 @@ __device__ __forceinline__ void prefetch_ckpt(const ReplayArgs& a, int item, boo
 }
 
 // One item's ring rows while they are in flight: up to K k-row and V v-row
-// passes per thread (a pass is nthr / (dk / 4) k rows or 16 v rows), the
+// passes per thread (a pass is nthr / (dk / 4) k rows or nthr / (dv / 4) v rows), the
 // thread's float4 of the drafts' q, and its alpha / beta. Rows beyond the
 // passes go through the tail loop of store_records, which waits for each row.
-// With dk = 128 and dv >= 64 two k passes and one v pass cover 16 rows. (Every
+// With dk = 128 and dv >= 64 two k passes and one v pass cover 16 rows (two v
+// passes with two tiles per wavefront, whose workgroup is half as large). (Every
 // pass is issued whether or not its rows exist, which keeps the compiler's
 // memory waits exact but costs a request per pass: three k and two v passes
 // for the verify kernels measured slower than the tail loop they save.)
-template <int TMAX>
+template <int TMAX, int VP = 1>
 struct RecRegs {
-  static constexpr int K = 2, V = 1;
+  static constexpr int K = 2, V = VP;
   f32x4 kb[K], vb[V], qv;
   f32x4 ab[K];  // KDA: the gate rows, staged like the k rows (unused by the other kinds)
   float al, be;
 };
 
 // Where a thread's share of the ring rows lies (k rows: LPR threads per row;
-// v rows: dv / 4 threads per row, 16 rows per pass since nthr = 4 dv).
+// v rows: dv / 4 threads per row, vstep rows per pass: 16 with one wavefront per
+// 16-row tile, 8 with two tiles per wavefront).
 struct StageMap {
-  int kstep, rk0, ck, rv0, cv;
+  int kstep, rk0, ck, rv0, cv, vstep;
   __device__ __forceinline__ StageMap(int tid, int nthr, int lpr, int dv) {
     kstep = nthr / lpr;
     rk0 = tid / lpr;
@@ -112,6 +114,7 @@ struct StageMap {
     const int dv4 = dv >> 2;
     rv0 = tid / dv4;
     cv = tid - rv0 * dv4;
+    vstep = nthr / dv4;
   }
 };
 
@@ -150,11 +153,11 @@ __device__ __forceinline__ RowSrc row_src(const ReplayArgs& a, const Item& it, i
   return s;
 }
 
-template <int KIND, int NT, int TMAX, bool FUSED>
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
 __device__ __forceinline__ void load_records(const ReplayArgs& a, const Item& item, const SeqPtr& p,
                                              const Route& rt, bool valid, int tid, const StageMap& m,
-                                             RecRegs<TMAX>& rr) {
-  constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
+                                             RecRegs<TMAX, RT>& rr) {
+  constexpr int kRecK = RecRegs<TMAX, RT>::K, kRecV = RecRegs<TMAX, RT>::V;
   constexpr int DK = NT * 16;
   // Every load is issued; one with nothing to fetch reads the first element of a
   // ring array (always allocated: q and the inputs are NULL in a flush call).
@@ -181,7 +184,7 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, const Item& it
   const bool raw = exact_fold<KIND>(rt);
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
-    const int r = m.rv0 + j * 16;
+    const int r = m.rv0 + j * m.vstep;
     const float* src = (fused && r >= p.h) ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
                                            : (raw && r < p.h ? s.rvraw : s.rv) + ring_slot(p.head, r, C) * dv + 4 * m.cv;
     rr.vb[j] = ld4(r < R ? src : a.ring_v);
@@ -204,11 +207,11 @@ __device__ __forceinline__ void load_records(const ReplayArgs& a, const Item& it
 // register passes straight from HBM.
 // A fused call also writes the drafts' records into their ring slots (k,
 // alpha, and v for Mamba-2 / beta for GDN, whose u replaces v later).
-template <int KIND, int NT, int TMAX, bool FUSED>
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
 __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, const ReplayLds& lds,
                                               const Item& item, const SeqPtr& p, const Route& rt, int tid,
-                                              int nthr, const StageMap& m, const RecRegs<TMAX>& rr) {
-  constexpr int kRecK = RecRegs<TMAX>::K, kRecV = RecRegs<TMAX>::V;
+                                              int nthr, const StageMap& m, const RecRegs<TMAX, RT>& rr) {
+  constexpr int kRecK = RecRegs<TMAX, RT>::K, kRecV = RecRegs<TMAX, RT>::V;
   constexpr int DK = NT * 16;
   constexpr bool GDN = kind_gdn(KIND);
   const bool raw = exact_fold<KIND>(rt);
@@ -231,7 +234,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
       if (in) st4(ra, y);
     }
   }
-  for (int r = m.rv0 + kRecV * 16; r < R; r += 16) {
+  for (int r = m.rv0 + kRecV * m.vstep; r < R; r += m.vstep) {
     const int slot = ring_slot(p.head, r, C);
     const bool in = fused && r >= p.h;
     const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
@@ -270,7 +273,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   }
 #pragma unroll
   for (int j = 0; j < kRecV; ++j) {
-    const int r = m.rv0 + j * 16;
+    const int r = m.rv0 + j * m.vstep;
     if (r < R) {
       st4(sm + lds.v + r * lds.dvs + 4 * m.cv, rr.vb[j]);
       if (!GDN && fused && r >= p.h) st4(wv + ring_slot(p.head, r, C) * dv + 4 * m.cv, rr.vb[j]);
@@ -297,11 +300,11 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
 // route reads, and rr its ring rows; both were requested during the previous
 // item. On return rr holds (or is loading) the rows of `next` and S its
 // checkpoint copy. Ends with a workgroup barrier after its last LDS read.
-template <int KIND, int NT, int TMAX, bool FUSED>
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
 __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, const ReplayLds& lds,
                                             const StageMap& map0, const Item it, const SeqPtr ptr, const Route rt,
-                                            f32x4 (&S)[NT], RecRegs<TMAX>& rr, const Item nit, const SeqPtr nptr,
-                                            const Route nrt) {
+                                            f32x4 (&S)[RT * NT], RecRegs<TMAX, RT>& rr, const Item nit,
+                                            const SeqPtr nptr, const Route nrt) {
   constexpr int DK = NT * 16;
   // Dot phase: each lane takes CPL float4 chunks of a k row (chunks li and
   // li + LPR), so LPR lanes share a row and a wavefront pass covers RPI rows.
@@ -312,6 +315,7 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   constexpr int RPI = kWave / LPR;
   constexpr bool GDN = kind_gdn(KIND);
   constexpr bool KDA = KIND == REPLAYSSM_KDA;
+  static_assert(RT == 1 || KIND != kKindGdnExact, "the exact-correction fold keeps one tile per wavefront");
 
   // The thread index is laundered per item: without it the compiler hoists
   // every thread-derived address out of the item loop and keeps them all live
@@ -328,7 +332,10 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int b = it.b;
   const int hd = it.hd;
   const int64_t bh = (int64_t)b * H + hd;
-  const int prow = wave * 16 + col;  // the state row this lane owns
+  // RT 16-row tiles per wavefront: the lane owns state rows prow + 16 tl, tl < RT
+  const int prow = wave * RT * 16 + col;
+  using Tile = f32x4[NT];
+  auto tile = [&](int tl) -> Tile& { return *reinterpret_cast<Tile*>(&S[tl * NT]); };
   // (the staging map is computed once per workgroup and laundered like tid)
   StageMap map = map0;
   __asm__ volatile("" : "+v"(map.rk0), "+v"(map.ck), "+v"(map.rv0), "+v"(map.cv));
@@ -346,12 +353,12 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   const int R = rt.R, r0 = rt.r0;
 
   // ---- 1. records (the checkpoint copy is already in flight) --------------------
-  if (work) store_records<KIND, NT, TMAX, FUSED>(a, sm, lds, it, ptr, rt, tid, nthr, map, rr);
+  if (work) store_records<KIND, NT, TMAX, FUSED, RT>(a, sm, lds, it, ptr, rt, tid, nthr, map, rr);
   __syncthreads();
 
   // ---- the next item's ring rows: requested now, waited for by the next item
   const bool more = nit.id < a.B * a.H;
-  load_records<KIND, NT, TMAX, FUSED>(a, nit, nptr, nrt, more, tid, map, rr);
+  load_records<KIND, NT, TMAX, FUSED, RT>(a, nit, nptr, nrt, more, tid, map, rr);
 
   // ---- KDA: the gate products, per channel (a thread per channel and job) ------
   // With per-channel gates the state after records [0, m] is
@@ -393,19 +400,24 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // pending when S is reloaded, so the compiler's waits before the reload stay at zero.
   auto prefetch_next = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) __asm__ volatile("" ::"v"(S[nt]));
-    prefetch_ckpt<NT>(a, nit.id, nrt.fold, more && nrt.work, wave, lane, S);
+    for (int nt = 0; nt < RT * NT; ++nt) __asm__ volatile("" ::"v"(S[nt]));
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl)
+      prefetch_ckpt<NT>(a, nit.id, nrt.fold, more && nrt.work, wave * RT + tl, lane, tile(tl));
   };
   const bool lp = reads_lp(prec, fold);
 
   // ---- matvecs y_i = S q_i (and S k_i for GDN), lane-partial over its columns.
   // A replay item does them right away, which frees S for the next item's
   // checkpoint. A fold item does them on the folded state, further down.
-  float yq[TMAX], yk[TMAX];
+  float yq[RT][TMAX], yk[RT][TMAX];
 #pragma unroll
-  for (int i = 0; i < TMAX; ++i) {
-    yq[i] = 0.f;
-    yk[i] = 0.f;
+  for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+    for (int i = 0; i < TMAX; ++i) {
+      yq[tl][i] = 0.f;
+      yk[tl][i] = 0.f;
+    }
   }
   auto matvec = [&]() {
 #pragma unroll
@@ -415,8 +427,14 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         if (i < T) {
           const float* qi = KDA ? sm + lds.qg + i * DK : sm + lds.q + i * DK;
           const float* ki = KDA ? sm + lds.kg + i * DK : sm + lds.k + (hc + i) * lds.dks;
-          yq[i] = fma4(S[nt], ld4(qi + nt * 16 + 4 * g), yq[i]);
-          if (GDN) yk[i] = fma4(S[nt], ld4(ki + nt * 16 + 4 * g), yk[i]);
+          const f32x4 qv = ld4(qi + nt * 16 + 4 * g);
+          f32x4 kv = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (GDN) kv = ld4(ki + nt * 16 + 4 * g);
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl) {
+            yq[tl][i] = fma4(S[tl * NT + nt], qv, yq[tl][i]);
+            if (GDN) yk[tl][i] = fma4(S[tl * NT + nt], kv, yk[tl][i]);
+          }
         }
       }
     }
@@ -616,9 +634,9 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   auto fold_state = [&]() {
     if constexpr (KIND == kKindGdnExact) {
       exact_fold_state();
-      if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, S);
+      if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, tile(0));
       if constexpr (NT >= 2) {
-        if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, S, prec == REPLAYSSM_BF16_SHARED);
+        if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, tile(0), prec == REPLAYSSM_BF16_SHARED);
       }
       return;
     }
@@ -628,26 +646,35 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       gf = suffix_product64((lane < hc) ? sm[lds.alpha + lane] : 1.f, lane);
       const float G = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gf), 0));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[nt] *= G;
+      for (int nt = 0; nt < RT * NT; ++nt) S[nt] *= G;
     }
-    // MFMA 16x16x4: A[m][kk] = k_j[16 nt + m], B[kk][n] = gamma_j v_j[16 wave + n],
+    // MFMA 16x16x4 per tile tl: A[m][kk] = k_j[16 nt + m], B[kk][n] = gamma_j v_j[prow - col + 16 tl + n],
     // j = 4 kc + kk; lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15].
     const int nkc = (hc + 3) >> 2;
     for (int kc = 0; kc < nkc; ++kc) {
       const int j = 4 * kc + g;
       const bool vj = j < hc;
       const float wj = KDA ? 1.f : __shfl(gf, (j + 1) & (kWave - 1), kWave);  // gf_{j+1}; j + 1 = 64 only if hc = 64
-      const float bval = vj ? (j + 1 < kWave ? wj : 1.f) * sm[lds.v + j * lds.dvs + prow] : 0.f;
+      float bval[RT];
+#pragma unroll
+      for (int tl = 0; tl < RT; ++tl)
+        bval[tl] = vj ? (j + 1 < kWave ? wj : 1.f) * sm[lds.v + j * lds.dvs + prow + 16 * tl] : 0.f;
       const float* krow = sm + lds.k + (vj ? j : 0) * lds.dks + col;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float aval = vj ? krow[nt * 16] : 0.f;
-        S[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval, S[nt], 0, 0, 0);
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl)
+          S[tl * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval[tl], S[tl * NT + nt], 0, 0, 0);
       }
     }
-    if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, S);
-    if constexpr (NT >= 2) {
-      if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, S, prec == REPLAYSSM_BF16_SHARED);
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl) {
+      if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave * RT + tl, lane, tile(tl));
+      if constexpr (NT >= 2) {
+        if (prec != REPLAYSSM_FP32)
+          store_lp<NT>(a.lp + hoff, wave * RT + tl, lane, tile(tl), prec == REPLAYSSM_BF16_SHARED);
+      }
     }
   };
 
@@ -694,53 +721,65 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     const float* gk = sm + lds.gk;
     const float* cq = sm + lds.cq;
     const float* ck = sm + lds.ck;
-    const float* sv = sm + lds.v + prow;
+    const float* sv = sm + lds.v + prow;  // tile tl's value at sv[16 tl]
     float* obase = a.out + ((int64_t)b * T * H + hd) * dv + prow;  // draft 0; draft i is i H dv further
     const int64_t ostep = (int64_t)H * dv;
-    float oc[TMAX];
+    float oc[RT][TMAX];
     if constexpr (!GDN) {
       // every staged record r0 .. R - 1 in one pass; the decay rows are zero for
       // records after a draft's end point
       float q0[TMAX];
       row(gq + r0 * TMAX, q0);
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i) oc[i] = q0[i] * yq[i];
+      for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) oc[tl][i] = q0[i] * yq[tl][i];
       for (int r = r0 + g; r < R; r += 4) {
         float w[TMAX], c[TMAX];
         row(gq + (r + 1) * TMAX, w);
         row(cq + r * TMAX, c);
-        const float u = sv[r * lds.dvs];
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i) oc[i] += w[i] * c[i] * u;
+        for (int tl = 0; tl < RT; ++tl) {
+          const float u = sv[r * lds.dvs + 16 * tl];
+#pragma unroll
+          for (int i = 0; i < TMAX; ++i) oc[tl][i] += w[i] * c[i] * u;
+        }
       }
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i)
-        if (i < T) oc[i] = sum_groups(oc[i]);
+      for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i)
+          if (i < T) oc[tl][i] = sum_groups(oc[tl][i]);
     } else {
       // committed records in parallel over the four lane groups (KDA: every
       // decay factor is 1, the gates being on the staged vectors)
-      float wc[TMAX];
+      float wc[RT][TMAX];
       if constexpr (KDA) {
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-          wc[i] = yk[i];
-          oc[i] = yq[i];
+        for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+          for (int i = 0; i < TMAX; ++i) {
+            wc[tl][i] = yk[tl][i];
+            oc[tl][i] = yq[tl][i];
+          }
         }
       } else {
         float k0[TMAX], q0[TMAX];
         row(gk + r0 * TMAX, k0);
         row(gq + r0 * TMAX, q0);
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-          wc[i] = k0[i] * yk[i];
-          oc[i] = q0[i] * yq[i];
+        for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+          for (int i = 0; i < TMAX; ++i) {
+            wc[tl][i] = k0[i] * yk[tl][i];
+            oc[tl][i] = q0[i] * yq[tl][i];
+          }
         }
       }
       for (int r = r0 + g; r < hc; r += 4) {
         float kc[TMAX], qc[TMAX];
         row(ck + r * TMAX, kc);
         row(cq + r * TMAX, qc);
-        const float u = sv[r * lds.dvs];
         if constexpr (!KDA) {
           float kw[TMAX], qw[TMAX];
           row(gk + (r + 1) * TMAX, kw);
@@ -752,28 +791,38 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
           }
         }
 #pragma unroll
-        for (int i = 0; i < TMAX; ++i) {
-          wc[i] += kc[i] * u;
-          oc[i] += qc[i] * u;
+        for (int tl = 0; tl < RT; ++tl) {
+          const float u = sv[r * lds.dvs + 16 * tl];
+#pragma unroll
+          for (int i = 0; i < TMAX; ++i) {
+            wc[tl][i] += kc[i] * u;
+            oc[tl][i] += qc[i] * u;
+          }
         }
       }
 #pragma unroll
-      for (int i = 0; i < TMAX; ++i) {
-        if (i < T) {
-          wc[i] = sum_groups(wc[i]);
-          oc[i] = sum_groups(oc[i]);
+      for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+        for (int i = 0; i < TMAX; ++i) {
+          if (i < T) {
+            wc[tl][i] = sum_groups(wc[tl][i]);
+            oc[tl][i] = sum_groups(oc[tl][i]);
+          }
         }
       }
       // drafts in order: u_d needs the corrections of the drafts before it; once
       // u_d is known it enters the sums of the drafts after it
-      float ud[TMAX];
+      float ud[RT][TMAX];
 #pragma unroll
       for (int d = 0; d < TMAX; ++d) {
-        ud[d] = 0.f;
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl) ud[tl][d] = 0.f;
         if (d < T) {
           const float al = KDA ? 1.f : sm[lds.alpha + hc + d];
           const float be = sm[lds.beta + hc + d];
-          ud[d] = be * (sv[(hc + d) * lds.dvs] - al * wc[d]);
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl)
+            ud[tl][d] = be * (sv[(hc + d) * lds.dvs + 16 * tl] - al * wc[tl][d]);
           float kc[TMAX], qc[TMAX];
           row(ck + (hc + d) * TMAX, kc);
           row(cq + (hc + d) * TMAX, qc);
@@ -788,9 +837,12 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
             }
           }
 #pragma unroll
-          for (int j = d; j < TMAX; ++j) {
-            if (j > d) wc[j] += kc[j] * ud[d];
-            oc[j] += qc[j] * ud[d];
+          for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+            for (int j = d; j < TMAX; ++j) {
+              if (j > d) wc[tl][j] += kc[j] * ud[tl][d];
+              oc[tl][j] += qc[j] * ud[tl][d];
+            }
           }
         }
       }
@@ -801,14 +853,19 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
         if (i < T) {
           int slot = head + hc + i;
           if (slot >= C) slot -= C;
-          a.ring_v[(bh * C + slot) * dv + prow] = pick(ud, i0);
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl) a.ring_v[(bh * C + slot) * dv + prow + 16 * tl] = pick(ud[tl], i0);
         }
       }
     }
 #pragma unroll
     for (int i0 = 0; i0 < TMAX; i0 += 4) {
       const int i = i0 + g;
-      if (i < T) __builtin_nontemporal_store(pick(oc, i0), obase + i * ostep);
+      if (i < T) {
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl)
+          __builtin_nontemporal_store(pick(oc[tl], i0), obase + i * ostep + 16 * tl);
+      }
     }
   }
   };
@@ -818,13 +875,18 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // point on every route: the compiler's waits are computed over every
   // control-flow path, and a path without the request would make them drain.
   if constexpr (NT >= 2) {
-    if (lp) widen_lp<NT>(S);  // (the shared-bf16 mode also folds from the bf16 values)
+    if (lp) {  // (the shared-bf16 mode also folds from the bf16 values)
+#pragma unroll
+      for (int tl = 0; tl < RT; ++tl) widen_lp<NT>(tile(tl));
+    }
   }
   if constexpr (KDA) {
     // S Diag(pf): the checkpoint carried over the committed records' gates
     if (work && hc > 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[nt] *= ld4(sm + lds.pf + nt * 16 + 4 * g);
+      for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[tl * NT + nt] *= ld4(sm + lds.pf + nt * 16 + 4 * g);
     }
   }
   if (fold) fold_state();
@@ -877,8 +939,10 @@ __device__ __forceinline__ void commit_pointers(const ReplayArgs& a, int tid, in
   }
 }
 
-template <int KIND, int NT, int TMAX, bool FUSED>
-__global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
+// (dv <= 256: a workgroup is at most 1024 / RT threads, which also bounds the
+// registers the compiler may give a thread)
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
+__global__ void __launch_bounds__(1024 / RT) replay_kernel(const ReplayArgs a) {
   extern __shared__ f32x4 smem_v4[];
   float* sm = reinterpret_cast<float*>(smem_v4);
   const int items = a.B * a.H;
@@ -910,8 +974,8 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   Route rt = route_of(a, ptr);
   const bool any = (int)blockIdx.x < items;
   if (!any) rt.work = false;
-  f32x4 S[NT];
-  RecRegs<TMAX> rr;
+  f32x4 S[RT * NT];
+  RecRegs<TMAX, RT> rr;
   // Loop invariants of the workgroup: the LDS carve-up and where a thread's
   // share of the ring rows lies.
   const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
@@ -929,15 +993,21 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
     return n;
   };
   Item it{(int)blockIdx.x, (int)blockIdx.x / H, (int)blockIdx.x % H};
-  load_records<KIND, NT, TMAX, FUSED>(a, it, ptr, rt, any, threadIdx.x, map, rr);
-  prefetch_ckpt<NT>(a, it.id, rt.fold, any && rt.work, wave, lane, S);
+  load_records<KIND, NT, TMAX, FUSED, RT>(a, it, ptr, rt, any, threadIdx.x, map, rr);
+  {
+    using Tile = f32x4[NT];
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl)
+      prefetch_ckpt<NT>(a, it.id, rt.fold, any && rt.work, wave * RT + tl, lane,
+                        *reinterpret_cast<Tile*>(&S[tl * NT]));
+  }
   for (int k = 0; it.id < items; ++k) {
     const Item nit = advance(it);
     const int kn = (k + 1) & 63;
     if (kn == 0 && nit.id < items) batch(nit.id);
     const SeqPtr nptr = ptr_at(kn);
     const Route nrt = route_of(a, nptr);
-    replay_item<KIND, NT, TMAX, FUSED>(a, sm, lds, map, it, ptr, rt, S, rr, nit, nptr, nrt);
+    replay_item<KIND, NT, TMAX, FUSED, RT>(a, sm, lds, map, it, ptr, rt, S, rr, nit, nptr, nrt);
     it = nit;
     ptr = nptr;
     rt = nrt;
@@ -954,23 +1024,38 @@ __global__ void __launch_bounds__(1024) replay_kernel(const ReplayArgs a) {
   if (flag[0]) commit_pointers(a, threadIdx.x, blockDim.x);
 }
 
-template <int KIND, int NT, int TMAX, bool FUSED>
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
 static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
   const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
-  const int block = a.dv / 16 * kWave;
+  const int block = a.dv / (16 * RT) * kWave;
   const size_t smem = (size_t)lds.total * 4;
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED>), block,
+  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>), block,
                                  smem, a.B * a.H, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED>), dim3((unsigned)grid), dim3((unsigned)block), smem,
+  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED, RT>), dim3((unsigned)grid), dim3((unsigned)block), smem,
                      s, a);
   return hipGetLastError();
 }
 
+// Gated DeltaNet with dk = 128 and at most four drafts: two 16-row tiles per
+// wavefront, so that the per-record factor rows read from LDS, the staged q / k
+// chunks of the mat-vecs and the lane-group reductions' setup serve 32 state
+// rows instead of 16, at twice the state registers.
+template <int KIND, int NT, int TMAX>
+constexpr bool kTwoTiles = KIND != kKindGdnExact && NT == 8 && TMAX <= 4;
+
+template <int KIND, int NT, int TMAX, int RT>
+static hipError_t launch_r(const ReplayArgs& a, hipStream_t s) {
+  return a.fused ? launch_t<KIND, NT, TMAX, true, RT>(a, s) : launch_t<KIND, NT, TMAX, false, RT>(a, s);
+}
+
 template <int KIND, int NT, int TMAX>
 static hipError_t launch_f(const ReplayArgs& a, hipStream_t s) {
-  return a.fused ? launch_t<KIND, NT, TMAX, true>(a, s) : launch_t<KIND, NT, TMAX, false>(a, s);
+  if constexpr (kTwoTiles<KIND, NT, TMAX>) {
+    if (a.dv % 32 == 0) return launch_r<KIND, NT, TMAX, 2>(a, s);
+  }
+  return launch_r<KIND, NT, TMAX, 1>(a, s);
 }
 
 template <int KIND, int NT>

@@ -169,3 +169,16 @@ def test_spec_rounds_wide_and_odd_heads(kind, P, N, T, L):
     rep = run_spec(r, T, 20)
     _assert_clean(rep)
     assert rep.folds > 0
+
+
+@pytest.mark.parametrize("P", [32, 96, 160])
+@pytest.mark.parametrize("T,L,fused", [(1, 4, False), (1, 6, True), (4, 9, False), (3, 5, True)])
+def test_gdn_two_tiles_per_wavefront(P, T, L, fused):
+    """Gated DeltaNet with dk = 128 and at most four drafts runs two 16-row tiles per
+    wavefront: one wavefront (dv = 32), an odd wavefront count (dv = 96, 160), decode and
+    speculative rounds, fused and from the ring, with folds."""
+    sh = LayerShape("gdn", 3, 3, P, 128)
+    r = Runner(sh, L, T, wid=170 + T, decay="slow")
+    rep = run_standard(r, 2 * L + 5, fused=fused) if T == 1 else run_spec(r, T, 20, fused=fused)
+    _assert_clean(rep)
+    assert rep.folds > 0
