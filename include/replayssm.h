@@ -380,6 +380,24 @@ int replayssm_conv_step(const replayssm_conv_config* cfg, const replayssm_conv_s
 int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv_state* st,
                           const int32_t* accepted, void* stream);
 
+/* ---- Kernel tiling (no effect on results) ----------------------------------------------
+ * How the replay kernel (decode, verify, flush and the fused steps) maps the checkpoint onto
+ * wavefronts when dk = 128, T_max <= 4 and dv is a multiple of 32 (the exact-correction fold
+ * of Gated DeltaNet with the two-precision checkpoint always uses one tile): one 16-row tile
+ * per wavefront, or two (half as many wavefronts per (sequence, head), more heads in flight
+ * per compute unit). Both give the same bits in every output, copy and ring; the choice only
+ * changes speed. REPLAYSSM_TILES_AUTO (the default) takes two tiles once a call has at least
+ * 8 (dv >= 128) or 64 (dv < 128) (sequence, head) items per compute unit of the current
+ * device, where their throughput was measured higher, and one tile for smaller batches, whose
+ * latency one tile keeps lower. Process-wide; takes effect at the next launch. EINVAL for
+ * another value. */
+#define REPLAYSSM_TILES_AUTO 0
+#define REPLAYSSM_TILES_ONE 1
+#define REPLAYSSM_TILES_TWO 2
+int replayssm_set_tiling(int policy);
+/* The current policy (one of the values above). */
+int replayssm_get_tiling(void);
+
 /* ---- Measurement helper (not a step of the method) -------------------------------------
  * Reads `bytes` bytes at device address `src` once, in the access pattern of the replay
  * kernel's checkpoint stream (persistent workgroups, 32 KiB per workgroup per pass, 16-byte

@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     ReplaySSMError, SIGNATURES, STRING_FUNCTIONS, LIB_PATH, State, Sizes, accept, append, append_dt, decode, decode_step,
     eager_accept, eager_step, eager_verify, flush, flush_selected, get_sizes, init, last_error, lib, make_config,
     pack_state, probe_read, read_error, restore, snapshot, status_string, unpack_state, verify, verify_step,
+    TILES_AUTO, TILES_ONE, TILES_TWO, get_tiling, set_tiling,
     ConvConfig, ConvLayer, ConvState, conv_accept, conv_init, conv_sizes, conv_step, make_conv_config,
 )

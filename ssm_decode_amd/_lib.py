@@ -27,6 +27,7 @@ PRECISIONS = {"fp32": FP32, "fp32_hp_bf16_lp": FP32_HP_BF16_LP, "bf16_shared": B
 KINDS = {"mamba2": MAMBA2, "gdn": GDN, "kda": KDA}
 
 OK, EINVAL, ENOTSUP, EHIP = 0, -1, -2, -3
+TILES_AUTO, TILES_ONE, TILES_TWO = 0, 1, 2
 DEVERR_APPEND_OVERFLOW, DEVERR_PENDING, DEVERR_ACCEPT, DEVERR_CORRUPT, DEVERR_STALE, DEVERR_INDEX = 1, 2, 4, 8, 16, 32
 
 _i32 = ctypes.c_int32
@@ -92,6 +93,8 @@ SIGNATURES = {
     "replayssm_eager_verify": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "replayssm_eager_accept": [ctypes.POINTER(Config), _vp, _vp, ctypes.c_int, _vp],
     "replayssm_probe_read": [_vp, ctypes.c_int64, _vp, _vp],
+    "replayssm_set_tiling": [ctypes.c_int],
+    "replayssm_get_tiling": [],
     "replayssm_flush_selected": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp],
     "replayssm_snapshot": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
     "replayssm_restore": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp],
@@ -255,6 +258,15 @@ def snapshot(cfg, st, seqs, dst, stream=None):
 def restore(cfg, st, seqs, src, stream=None):
     _check(lib().replayssm_restore(ctypes.byref(cfg), ctypes.byref(st), int(seqs.numel()), _i32t(seqs), _f32(src),
                                    _s(stream)), "restore")
+
+
+def set_tiling(policy):
+    """replayssm_set_tiling: TILES_AUTO, TILES_ONE or TILES_TWO (process-wide; results unchanged)."""
+    _check(lib().replayssm_set_tiling(int(policy)), "set_tiling")
+
+
+def get_tiling():
+    return int(lib().replayssm_get_tiling())
 
 
 def probe_read(src, sink, stream=None):

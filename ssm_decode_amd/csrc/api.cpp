@@ -470,6 +470,15 @@ int replayssm_eager_accept(const replayssm_config* cfg, int32_t* slot, const int
                     "eager_accept");
 }
 
+int replayssm_set_tiling(int policy) {
+  if (policy != REPLAYSSM_TILES_AUTO && policy != REPLAYSSM_TILES_ONE && policy != REPLAYSSM_TILES_TWO)
+    return fail(REPLAYSSM_EINVAL, "tiling policy %d is not one of 0 (auto), 1 (one tile), 2 (two tiles)", policy);
+  rs::set_tiling(policy);
+  return REPLAYSSM_OK;
+}
+
+int replayssm_get_tiling(void) { return rs::get_tiling(); }
+
 int replayssm_probe_read(const void* src, int64_t bytes, float* sink, void* stream) {
   NEED(src);
   if (sink == nullptr) return fail(REPLAYSSM_EINVAL, "sink is NULL");

@@ -154,6 +154,11 @@ hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items
 
 // Launchers (one per kernel family); they return hipError_t of the launch.
 hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStream_t s);
+// Tiling policy of the replay kernel (REPLAYSSM_TILES_*), process-wide.
+void set_tiling(int policy);
+int get_tiling();
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus);
 hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s);
 hipError_t launch_accept(int32_t* h, int32_t* p, int32_t* err, const int32_t* acc, int B, int L,
                          hipStream_t s);

@@ -45,6 +45,8 @@
 // checkpoint request at one program point: the next item then waits for its
 // records without waiting for its checkpoint, and for its checkpoint without
 // waiting for the records requested after it.
+#include <atomic>
+
 #include "route.hpp"
 
 namespace rs {
@@ -1038,12 +1040,39 @@ static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Gated DeltaNet with dk = 128 and at most four drafts: two 16-row tiles per
-// wavefront, so that the per-record factor rows read from LDS, the staged q / k
-// chunks of the mat-vecs and the lane-group reductions' setup serve 32 state
-// rows instead of 16, at twice the state registers.
+// dk = 128 with at most four drafts: two 16-row tiles per wavefront, so that the
+// per-record factor rows read from LDS, the staged q / k chunks of the mat-vecs,
+// the scans and the dot passes serve 32 state rows instead of 16, at twice the
+// state registers. Each row's arithmetic is the same in both forms (same lanes,
+// same order), so the results are bit-identical.
 template <int KIND, int NT, int TMAX>
 constexpr bool kTwoTiles = KIND != kKindGdnExact && NT == 8 && TMAX <= 4;
+
+std::atomic<int> g_tiling{REPLAYSSM_TILES_AUTO};
+
+void set_tiling(int policy) { g_tiling.store(policy, std::memory_order_relaxed); }
+int get_tiling() { return g_tiling.load(std::memory_order_relaxed); }
+
+// Automatic choice: two tiles once the batch fills the device (their occupancy
+// holds more heads in flight per compute unit), one below that (a head's work
+// spread over twice the wavefronts finishes sooner). Thresholds from B-sweeps on
+// MI355X: Mamba-2 64x128 (dv = 64) breaks even at 64 items per CU, Gated DeltaNet
+// 128x128 (dv = 128) at 8.
+static hipError_t two_tiles(const ReplayArgs& a, bool* two) {
+  *two = false;
+  if (a.dv % 32 != 0) return hipSuccess;
+  const int policy = get_tiling();
+  if (policy != REPLAYSSM_TILES_AUTO) {
+    *two = policy == REPLAYSSM_TILES_TWO;
+    return hipSuccess;
+  }
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t per_cu = a.dv >= 128 ? 8 : 64;
+  *two = (int64_t)a.B * a.H >= per_cu * cus;
+  return hipSuccess;
+}
 
 template <int KIND, int NT, int TMAX, int RT>
 static hipError_t launch_r(const ReplayArgs& a, hipStream_t s) {
@@ -1053,7 +1082,10 @@ static hipError_t launch_r(const ReplayArgs& a, hipStream_t s) {
 template <int KIND, int NT, int TMAX>
 static hipError_t launch_f(const ReplayArgs& a, hipStream_t s) {
   if constexpr (kTwoTiles<KIND, NT, TMAX>) {
-    if (a.dv % 32 == 0) return launch_r<KIND, NT, TMAX, 2>(a, s);
+    bool two = false;
+    hipError_t e = two_tiles(a, &two);
+    if (e != hipSuccess) return e;
+    if (two) return launch_r<KIND, NT, TMAX, 2>(a, s);
   }
   return launch_r<KIND, NT, TMAX, 1>(a, s);
 }

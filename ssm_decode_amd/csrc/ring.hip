@@ -7,6 +7,22 @@
 
 namespace rs {
 
+hipError_t device_cus(int* cus) {
+  static std::mutex mu;
+  static int count[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (count[dev] == 0) {
+    e = hipDeviceGetAttribute(&count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  *cus = count[dev];
+  return hipSuccess;
+}
+
 hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid) {
   struct Entry {
     const void* kernel;

@@ -32,6 +32,10 @@ hipError_t launch_restore(float*, uint16_t*, int32_t*, int32_t*, int32_t*, int64
 hipError_t launch_eager(int, int, const EagerArgs&, hipStream_t) { return count(); }
 hipError_t launch_eager_accept(int32_t*, const int32_t*, int, int, hipStream_t) { return count(); }
 hipError_t launch_probe_read(const void*, int64_t, float*, hipStream_t) { return count(); }
+static int tiling = REPLAYSSM_TILES_AUTO;
+void set_tiling(int policy) { tiling = policy; }
+int get_tiling() { return tiling; }
+hipError_t device_cus(int* cus) { *cus = 256; return count(); }
 hipError_t launch_conv_init(const ConvArgs&, hipStream_t) { return count(); }
 hipError_t launch_conv_step(const ConvArgs&, hipStream_t) { return count(); }
 hipError_t launch_conv_accept(const ConvArgs&, const int32_t*, hipStream_t) { return count(); }
@@ -127,6 +131,12 @@ int main() {
   EXPECT(replayssm_get_sizes(nullptr, &sz), REPLAYSSM_EINVAL);
   EXPECT(replayssm_probe_read(F(40), 1 << 20, F(41), nullptr), REPLAYSSM_OK);
   EXPECT(replayssm_probe_read(F(40), 1000, F(41), nullptr), REPLAYSSM_EINVAL);
+  EXPECT(replayssm_set_tiling(REPLAYSSM_TILES_TWO), REPLAYSSM_OK);
+  EXPECT(replayssm_get_tiling(), REPLAYSSM_TILES_TWO);
+  EXPECT(replayssm_set_tiling(3), REPLAYSSM_EINVAL);
+  EXPECT(replayssm_set_tiling(-1), REPLAYSSM_EINVAL);
+  EXPECT(replayssm_get_tiling(), REPLAYSSM_TILES_TWO);
+  EXPECT(replayssm_set_tiling(REPLAYSSM_TILES_AUTO), REPLAYSSM_OK);
 
   // the convolution ring
   for (int W = 0; W <= 5; ++W)

@@ -186,3 +186,19 @@ def test_status_strings(rs):
     assert rs.status_string(-1) == "invalid argument"
     assert rs.status_string(-2) == "not supported"
     assert rs.status_string(-3) == "HIP runtime error"
+
+
+def test_tiling_policy(rs):
+    """The tiling switch is host state only: validated, stored, read back; no GPU needed."""
+    assert rs.get_tiling() == rs.TILES_AUTO
+    try:
+        for p in (rs.TILES_ONE, rs.TILES_TWO, rs.TILES_AUTO):
+            rs.set_tiling(p)
+            assert rs.get_tiling() == p
+        rs.set_tiling(rs.TILES_TWO)
+        for bad in (3, -1, 1 << 20):
+            assert rs.lib().replayssm_set_tiling(bad) == rs.EINVAL
+            assert "tiling policy" in rs.last_error()
+            assert rs.get_tiling() == rs.TILES_TWO
+    finally:
+        rs.set_tiling(rs.TILES_AUTO)

@@ -171,13 +171,21 @@ def test_spec_rounds_wide_and_odd_heads(kind, P, N, T, L):
     assert rep.folds > 0
 
 
+@pytest.fixture
+def two_tiles():
+    rs.set_tiling(rs.TILES_TWO)
+    yield
+    rs.set_tiling(rs.TILES_AUTO)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn", "kda"])
 @pytest.mark.parametrize("P", [32, 96, 160])
 @pytest.mark.parametrize("T,L,fused", [(1, 4, False), (1, 6, True), (4, 9, False), (3, 5, True)])
-def test_gdn_two_tiles_per_wavefront(P, T, L, fused):
-    """Gated DeltaNet with dk = 128 and at most four drafts runs two 16-row tiles per
-    wavefront: one wavefront (dv = 32), an odd wavefront count (dv = 96, 160), decode and
-    speculative rounds, fused and from the ring, with folds."""
-    sh = LayerShape("gdn", 3, 3, P, 128)
+def test_two_tiles_per_wavefront(kind, P, T, L, fused, two_tiles):
+    """dk = 128 with at most four drafts, two 16-row tiles per wavefront forced (the automatic
+    choice takes them only for large batches): one wavefront (dv = 32), an odd wavefront count
+    (dv = 96, 160), decode and speculative rounds, fused and from the ring, with folds."""
+    sh = LayerShape(kind, 3, 3, P, 128)
     r = Runner(sh, L, T, wid=170 + T, decay="slow")
     rep = run_standard(r, 2 * L + 5, fused=fused) if T == 1 else run_spec(r, T, 20, fused=fused)
     _assert_clean(rep)
