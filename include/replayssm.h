@@ -382,8 +382,7 @@ int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv
 
 /* ---- Kernel tiling (no effect on results) ----------------------------------------------
  * How the replay kernel (decode, verify, flush and the fused steps) maps the checkpoint onto
- * wavefronts when dk = 128, T_max <= 4 and dv is a multiple of 32 (the exact-correction fold
- * of Gated DeltaNet with the two-precision checkpoint always uses one tile): one 16-row tile
+ * wavefronts when dk = 128, T_max <= 4 and dv is a multiple of 32: one 16-row tile
  * per wavefront, or two (half as many wavefronts per (sequence, head), more heads in flight
  * per compute unit). Both give the same bits in every output, copy and ring; the choice only
  * changes speed. REPLAYSSM_TILES_AUTO (the default) takes two tiles once a call has at least

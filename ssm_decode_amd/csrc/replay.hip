@@ -317,7 +317,6 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   constexpr int RPI = kWave / LPR;
   constexpr bool GDN = kind_gdn(KIND);
   constexpr bool KDA = KIND == REPLAYSSM_KDA;
-  static_assert(RT == 1 || KIND != kKindGdnExact, "the exact-correction fold keeps one tile per wavefront");
 
   // The thread index is laundered per item: without it the compiler hoists
   // every thread-derived address out of the item loop and keeps them all live
@@ -589,33 +588,47 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     }
     for (int j0 = 0; j0 < hc; j0 += 4) {
       const int nb = hc - j0 < 4 ? hc - j0 : 4;
-      float w0[4];
+      float w0[RT][4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const float* kj = sm + lds.k + (jj < nb ? j0 + jj : 0) * lds.dks + 4 * g;
-        float part = 0.f;
+        float part[RT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) part = fma4(S[nt], ld4(kj + 16 * nt), part);
-        w0[jj] = part;
+        for (int tl = 0; tl < RT; ++tl) part[tl] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const f32x4 kv = ld4(kj + 16 * nt);
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl) part[tl] = fma4(S[tl * NT + nt], kv, part[tl]);
+        }
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl) w0[tl][jj] = part[tl];
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w0[jj] = sum_groups(w0[jj]);
-      float u[4];
+      for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w0[tl][jj] = sum_groups(w0[tl][jj]);
+      float u[RT][4];
       float D = 1.f;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        u[jj] = 0.f;
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl) u[tl][jj] = 0.f;
         if (jj < nb) {
           const int j = j0 + jj;
-          float w = D * w0[jj];
-          float gij = 1.f;
-#pragma unroll
-          for (int ii = jj - 1; ii >= 0; --ii) {
-            w += gij * sm[lds.gram + (j0 + ii) * C + j] * u[ii];
-            gij *= sm[lds.alpha + j0 + ii];
-          }
           const float al = sm[lds.alpha + j];
-          u[jj] = sm[lds.beta + j] * (sm[lds.v + j * lds.dvs + prow] - al * w);
+          const float be = sm[lds.beta + j];
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl) {
+            float w = D * w0[tl][jj];
+            float gij = 1.f;
+#pragma unroll
+            for (int ii = jj - 1; ii >= 0; --ii) {
+              w += gij * sm[lds.gram + (j0 + ii) * C + j] * u[tl][ii];
+              gij *= sm[lds.alpha + j0 + ii];
+            }
+            u[tl][jj] = be * (sm[lds.v + j * lds.dvs + prow + 16 * tl] - al * w);
+          }
           D *= al;
         }
       }
@@ -623,12 +636,19 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
       float ge = 1.f;
       for (int m = j0 + g + 1; m < j0 + nb; ++m) ge *= sm[lds.alpha + m];
       const bool vj = g < nb;
-      const float bval = vj ? ge * (g == 0 ? u[0] : g == 1 ? u[1] : g == 2 ? u[2] : u[3]) : 0.f;
+      float bval[RT];
+#pragma unroll
+      for (int tl = 0; tl < RT; ++tl)
+        bval[tl] = vj ? ge * (g == 0 ? u[tl][0] : g == 1 ? u[tl][1] : g == 2 ? u[tl][2] : u[tl][3]) : 0.f;
       const float* krow = sm + lds.k + (vj ? j0 + g : 0) * lds.dks + col;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        S[nt] *= D;
-        S[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vj ? krow[nt * 16] : 0.f, bval, S[nt], 0, 0, 0);
+        const float aval = vj ? krow[nt * 16] : 0.f;
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl) {
+          S[tl * NT + nt] *= D;
+          S[tl * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval[tl], S[tl * NT + nt], 0, 0, 0);
+        }
       }
     }
   };
@@ -636,9 +656,13 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   auto fold_state = [&]() {
     if constexpr (KIND == kKindGdnExact) {
       exact_fold_state();
-      if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave, lane, tile(0));
-      if constexpr (NT >= 2) {
-        if (prec != REPLAYSSM_FP32) store_lp<NT>(a.lp + hoff, wave, lane, tile(0), prec == REPLAYSSM_BF16_SHARED);
+#pragma unroll
+      for (int tl = 0; tl < RT; ++tl) {
+        if (prec != REPLAYSSM_BF16_SHARED) store_hp<NT>(a.hp + hoff, wave * RT + tl, lane, tile(tl));
+        if constexpr (NT >= 2) {
+          if (prec != REPLAYSSM_FP32)
+            store_lp<NT>(a.lp + hoff, wave * RT + tl, lane, tile(tl), prec == REPLAYSSM_BF16_SHARED);
+        }
       }
       return;
     }
@@ -1042,11 +1066,11 @@ static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
 
 // dk = 128 with at most four drafts: two 16-row tiles per wavefront, so that the
 // per-record factor rows read from LDS, the staged q / k chunks of the mat-vecs,
-// the scans and the dot passes serve 32 state rows instead of 16, at twice the
-// state registers. Each row's arithmetic is the same in both forms (same lanes,
+// the scans, the dot passes and (exact-correction fold) the Gram blocks serve 32
+// state rows instead of 16, at twice the state registers. Each row's arithmetic is the same in both forms (same lanes,
 // same order), so the results are bit-identical.
 template <int KIND, int NT, int TMAX>
-constexpr bool kTwoTiles = KIND != kKindGdnExact && NT == 8 && TMAX <= 4;
+constexpr bool kTwoTiles = NT == 8 && TMAX <= 4;
 
 std::atomic<int> g_tiling{REPLAYSSM_TILES_AUTO};
 
