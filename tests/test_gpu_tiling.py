@@ -80,3 +80,49 @@ def test_auto_policy_switches_by_batch(restore_tiling):
         ob, _ = _run("gdn", "fp32", sh, 4, 1, True, rs.TILES_ONE, 199, 6)
         oc, _ = _run("gdn", "fp32", sh, 4, 1, True, rs.TILES_TWO, 199, 6)
         assert torch.equal(oa, ob) and torch.equal(oa, oc)
+
+
+def _run_device(w, precision, T, policy, rounds):
+    """The full-size workload's layer on device-drawn inputs: decode steps (T = 1) or
+    speculative rounds (fused verify, then a drawn accept), with folds."""
+    import synth
+
+    rs.set_tiling(policy)
+    sh = w.shape
+    cfg = rs.make_config(sh.kind, precision, sh.B, sh.H, sh.P, sh.N, w.L, T)
+    lay = rs.LayerState(cfg)
+    lay.import_state(synth.device_initial_state(0, w.wid, sh, w.s0_sigma, "cuda"))
+    outs = torch.empty((rounds, sh.B, T, sh.H, sh.P), device="cuda")
+    for r in range(rounds):
+        x = synth.device_step(0, w.wid, 500 + r, sh, T, "cuda")
+        if T == 1:
+            rs.decode_step(cfg, lay.struct, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], outs[r])
+        else:
+            rs.verify_step(cfg, lay.struct, T, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], outs[r])
+            rs.accept(cfg, lay.struct, synth.device_accept(0, w.wid, 500 + r, sh.B, T, "cuda"))
+    torch.cuda.synchronize()
+    assert rs.read_error(lay.struct) == 0
+    return outs, lay
+
+
+@pytest.mark.parametrize("wname,precision,T", [("mamba2_decode_b256", "fp32", 1),
+                                                ("mamba2_decode_b256", "fp32_hp_bf16_lp", 4),
+                                                ("gdn_decode_b256", "fp32_hp_bf16_lp", 4),
+                                                ("kda_decode_b256", "fp32", 4)])
+def test_full_size_layers_bit_identical(wname, precision, T, restore_tiling):
+    """At the benchmark's B = 256 shapes (where the automatic choice is two tiles) the forced
+    one-tile kernels give the same bits: outputs of every round, both checkpoint copies after
+    the folds, rings and pointers."""
+    import synth
+
+    w = synth.WORKLOADS[wname]
+    rounds = 20 if T == 1 else 12
+    oa, la = _run_device(w, precision, T, rs.TILES_ONE, rounds)
+    ob, lb = _run_device(w, precision, T, rs.TILES_AUTO, rounds)
+    assert torch.equal(oa, ob)
+    for name in ("hp", "lp", "ring_alpha", "ring_beta", "ring_k", "ring_v", "ring_vraw", "head", "h", "p", "folded"):
+        ta, tb = getattr(la, name), getattr(lb, name)
+        if ta is not None:
+            assert torch.equal(ta, tb), name
+    assert la.pointers() == lb.pointers()
+    assert max(la.pointers()["folded"]) > 0
