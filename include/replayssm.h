@@ -386,9 +386,10 @@ int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv
  * per wavefront, or two (half as many wavefronts per (sequence, head), more heads in flight
  * per compute unit). Both give the same bits in every output, copy and ring; the choice only
  * changes speed. REPLAYSSM_TILES_AUTO (the default) takes two tiles once a call has at least
- * 8 (dv >= 128) or 64 (dv < 128) (sequence, head) items per compute unit of the current
- * device, where their throughput was measured higher, and one tile for smaller batches, whose
- * latency one tile keeps lower. Process-wide; takes effect at the next launch. EINVAL for
+ * 64 (dv < 128), 6 (dv >= 128) or 3 (dv >= 128, Gated DeltaNet with the two-precision
+ * checkpoint) (sequence, head) items per compute unit of the current device, where their
+ * throughput was measured higher, and one tile for smaller batches, whose latency one tile
+ * keeps lower. Process-wide; takes effect at the next launch. EINVAL for
  * another value. */
 #define REPLAYSSM_TILES_AUTO 0
 #define REPLAYSSM_TILES_ONE 1

@@ -1079,10 +1079,12 @@ int get_tiling() { return g_tiling.load(std::memory_order_relaxed); }
 
 // Automatic choice: two tiles once the batch fills the device (their occupancy
 // holds more heads in flight per compute unit), one below that (a head's work
-// spread over twice the wavefronts finishes sooner). Thresholds from B-sweeps on
-// MI355X: Mamba-2 64x128 (dv = 64) breaks even at 64 items per CU, Gated DeltaNet
-// 128x128 (dv = 128) at 8.
-static hipError_t two_tiles(const ReplayArgs& a, bool* two) {
+// spread over twice the wavefronts finishes sooner). Thresholds from B-sweeps of
+// decode and verify T = 4 on MI355X: Mamba-2 64x128 (dv = 64) breaks even at 64
+// items per CU, Gated DeltaNet and KDA 128x128 (dv = 128) at about 6, and the
+// exact-correction fold of Gated DeltaNet's two-precision checkpoint, whose fold
+// work the second tile shares, at about 3.
+static hipError_t two_tiles(const ReplayArgs& a, bool exact, bool* two) {
   *two = false;
   if (a.dv % 32 != 0) return hipSuccess;
   const int policy = get_tiling();
@@ -1093,7 +1095,7 @@ static hipError_t two_tiles(const ReplayArgs& a, bool* two) {
   int cus = 0;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  const int64_t per_cu = a.dv >= 128 ? 8 : 64;
+  const int64_t per_cu = a.dv < 128 ? 64 : exact ? 3 : 6;
   *two = (int64_t)a.B * a.H >= per_cu * cus;
   return hipSuccess;
 }
@@ -1107,7 +1109,7 @@ template <int KIND, int NT, int TMAX>
 static hipError_t launch_f(const ReplayArgs& a, hipStream_t s) {
   if constexpr (kTwoTiles<KIND, NT, TMAX>) {
     bool two = false;
-    hipError_t e = two_tiles(a, &two);
+    hipError_t e = two_tiles(a, KIND == kKindGdnExact, &two);
     if (e != hipSuccess) return e;
     if (two) return launch_r<KIND, NT, TMAX, 2>(a, s);
   }

@@ -71,7 +71,7 @@ def test_one_and_two_tiles_bit_identical(kind, precision, T, fused, restore_tili
 
 
 def test_auto_policy_switches_by_batch(restore_tiling):
-    """Automatic tiling on both sides of the switch point (8 items per compute unit at
+    """Automatic tiling on both sides of the switch point (6 items per compute unit at
     dv = 128) gives the bits of the forced tilings."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for B in (2, -(-8 * cus // 4)):
