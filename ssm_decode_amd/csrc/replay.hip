@@ -223,44 +223,7 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   constexpr bool fused = FUSED;
   float* wk = a.ring_k + (s.rk - a.ring_k);
   float* wv = a.ring_v + (s.rv - a.ring_v);
-  for (int r = m.rk0 + kRecK * m.kstep; r < R; r += m.kstep) {
-    const int slot = ring_slot(p.head, r, C);
-    const bool in = fused && r >= p.h;
-    const f32x4 x = ld4(in ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck : s.rk + slot * DK + 4 * m.ck);
-    st4(sm + lds.k + r * lds.dks + 4 * m.ck, x);
-    if (in) st4(wk + slot * DK + 4 * m.ck, x);
-    if constexpr (KIND == REPLAYSSM_KDA) {
-      float* ra = a.ring_alpha + (s.bhC + slot) * DK + 4 * m.ck;
-      const f32x4 y = ld4(in ? a.in_alpha + (s.ia + (int64_t)(r - p.h) * H) * DK + 4 * m.ck : ra);
-      st4(sm + lds.alpha + r * lds.dks + 4 * m.ck, y);
-      if (in) st4(ra, y);
-    }
-  }
-  for (int r = m.rv0 + kRecV * m.vstep; r < R; r += m.vstep) {
-    const int slot = ring_slot(p.head, r, C);
-    const bool in = fused && r >= p.h;
-    const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
-                           : (raw && r < p.h ? s.rvraw : s.rv) + slot * dv + 4 * m.cv);
-    st4(sm + lds.v + r * lds.dvs + 4 * m.cv, x);
-    if (in && !GDN) st4(wv + slot * dv + 4 * m.cv, x);
-    if (in && GDN && a.ring_vraw) st4(a.ring_vraw + (s.rv - a.ring_v) + slot * dv + 4 * m.cv, x);
-  }
-  for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
-    st4(sm + lds.q + i * DK + 4 * m.ck, ld4_stream(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
-  for (int r = tid + nthr; r < R; r += nthr) {
-    const int slot = ring_slot(p.head, r, C);
-    const bool in = fused && r >= p.h;
-    if constexpr (KIND != REPLAYSSM_KDA) {
-      const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
-      sm[lds.alpha + r] = al;
-      if (in) a.ring_alpha[s.bhC + slot] = al;
-    }
-    if (GDN && (r >= p.h || raw)) {
-      const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
-      sm[lds.beta + r] = be;
-      if (in) a.ring_beta[s.bhC + slot] = be;
-    }
-  }
+  // the register rows first: their registers are then free for the tail loads
 #pragma unroll
   for (int j = 0; j < kRecK; ++j) {
     const int r = m.rk0 + j * m.kstep;
@@ -294,6 +257,63 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
     if (GDN && (tid >= p.h || raw)) {
       sm[lds.beta + tid] = rr.be;
       if (fused && tid >= p.h) a.ring_beta[s.bhC + ring_slot(p.head, tid, C)] = rr.be;
+    }
+  }
+  // k rows past the register passes: kTail rows' loads issued together, then
+  // their stores (one memory round trip per group instead of one per row; no
+  // load of a group reads a slot that a store of the same group writes)
+  constexpr int kTail = KIND == REPLAYSSM_KDA ? 1 : 4;
+  for (int r0 = m.rk0 + kRecK * m.kstep; r0 < R; r0 += kTail * m.kstep) {
+    f32x4 x[kTail], y[kTail];
+#pragma unroll
+    for (int u = 0; u < kTail; ++u) {
+      const int r = r0 + u * m.kstep;
+      const bool in = fused && r >= p.h;
+      const int slot = ring_slot(p.head, r, C);
+      x[u] = ld4(r >= R ? a.ring_k : in ? s.ik + (int64_t)(r - p.h) * H * DK + 4 * m.ck : s.rk + slot * DK + 4 * m.ck);
+      if constexpr (KIND == REPLAYSSM_KDA)
+        y[u] = ld4(r >= R ? a.ring_alpha
+                          : in ? a.in_alpha + (s.ia + (int64_t)(r - p.h) * H) * DK + 4 * m.ck
+                               : a.ring_alpha + (s.bhC + slot) * DK + 4 * m.ck);
+    }
+#pragma unroll
+    for (int u = 0; u < kTail; ++u) {
+      const int r = r0 + u * m.kstep;
+      if (r < R) {
+        const bool in = fused && r >= p.h;
+        const int slot = ring_slot(p.head, r, C);
+        st4(sm + lds.k + r * lds.dks + 4 * m.ck, x[u]);
+        if (in) st4(wk + slot * DK + 4 * m.ck, x[u]);
+        if constexpr (KIND == REPLAYSSM_KDA) {
+          st4(sm + lds.alpha + r * lds.dks + 4 * m.ck, y[u]);
+          if (in) st4(a.ring_alpha + (s.bhC + slot) * DK + 4 * m.ck, y[u]);
+        }
+      }
+    }
+  }
+  for (int r = m.rv0 + kRecV * m.vstep; r < R; r += m.vstep) {
+    const int slot = ring_slot(p.head, r, C);
+    const bool in = fused && r >= p.h;
+    const f32x4 x = ld4(in ? s.iv + (int64_t)(r - p.h) * H * dv + 4 * m.cv
+                           : (raw && r < p.h ? s.rvraw : s.rv) + slot * dv + 4 * m.cv);
+    st4(sm + lds.v + r * lds.dvs + 4 * m.cv, x);
+    if (in && !GDN) st4(wv + slot * dv + 4 * m.cv, x);
+    if (in && GDN && a.ring_vraw) st4(a.ring_vraw + (s.rv - a.ring_v) + slot * dv + 4 * m.cv, x);
+  }
+  for (int i = m.rk0 + m.kstep; i < T; i += m.kstep)
+    st4(sm + lds.q + i * DK + 4 * m.ck, ld4_stream(a.q + (((int64_t)b * T + i) * H + hd) * DK + 4 * m.ck));
+  for (int r = tid + nthr; r < R; r += nthr) {
+    const int slot = ring_slot(p.head, r, C);
+    const bool in = fused && r >= p.h;
+    if constexpr (KIND != REPLAYSSM_KDA) {
+      const float al = in ? a.in_alpha[s.ia + (int64_t)(r - p.h) * H] : a.ring_alpha[s.bhC + slot];
+      sm[lds.alpha + r] = al;
+      if (in) a.ring_alpha[s.bhC + slot] = al;
+    }
+    if (GDN && (r >= p.h || raw)) {
+      const float be = in ? a.in_beta[s.ia + (int64_t)(r - p.h) * H] : a.ring_beta[s.bhC + slot];
+      sm[lds.beta + r] = be;
+      if (in) a.ring_beta[s.bhC + slot] = be;
     }
   }
 }
