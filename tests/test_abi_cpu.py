@@ -202,3 +202,15 @@ def test_tiling_policy(rs):
             assert rs.get_tiling() == rs.TILES_TWO
     finally:
         rs.set_tiling(rs.TILES_AUTO)
+
+
+def test_binding_constants_match_the_header(rs):
+    """Every status, device-error and tiling constant the binding mirrors has the header's value."""
+    text = open(HEADER).read()
+    defined = {m.group(1): int(m.group(2)) for m in
+               re.finditer(r"^#define REPLAYSSM_(\w+)\s+\(?(-?\d+)\)?", text, re.M)}
+    mirrored = [n for n in ("OK", "EINVAL", "ENOTSUP", "EHIP", "TILES_AUTO", "TILES_ONE", "TILES_TWO")]
+    mirrored += [n for n in defined if n.startswith("DEVERR_")]
+    for name in mirrored:
+        assert getattr(rs, name) == defined[name], name
+    assert {"TILES_AUTO", "TILES_ONE", "TILES_TWO", "DEVERR_INDEX"} <= set(defined)
