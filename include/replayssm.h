@@ -30,8 +30,11 @@
  *    leaves that sequence unchanged (or clamps, as documented per call) and ORs
  *    a REPLAYSSM_DEVERR_* bit into the sticky word `state->err`, which
  *    replayssm_read_error() returns.
- *  - The library is stateless: calls on distinct states may run concurrently;
- *    calls on one state must be stream-ordered.
+ *  - The library keeps no per-layer state: calls on distinct states may run
+ *    concurrently; calls on one state must be stream-ordered. Its only
+ *    process-wide state is the kernel tiling policy (replayssm_set_tiling,
+ *    shared by every thread and device; it never changes results) and the
+ *    per-device caches of compute-unit counts and kernel occupancies.
  *
  * Shapes use B sequences, H heads, dv = value/head dim (Mamba-2 P, GDN d_v),
  * dk = key/state dim (Mamba-2 N, GDN d_k), ring capacity C = L + T_max.
@@ -254,7 +257,13 @@ int replayssm_accept(const replayssm_config* cfg, const replayssm_state* st,
 /* Folds every committed record into the checkpoint now (a rank-h update,
  * written to HP and/or LP as the precision mode requires): head += h mod C,
  * folded += h, h = 0. Pending drafts are kept. Sequences with h = 0 are left
- * alone. Afterwards the checkpoint alone is the state at position `folded`. */
+ * alone. Afterwards the checkpoint alone is the state at position `folded`.
+ * This is the fold that decode and verify run on their flush route, on its
+ * own: the checkpoint becomes the decayed checkpoint plus the buffered records
+ * ("How it works": Standard decoding, the checkpoint is written when the buffer
+ * is folded; the author's reply on the flush route in the thread "Songlin Yang
+ * releases ReplaySSM": the new state is one product of the stacked v and k
+ * vectors, V K^T, instead of a token-by-token recurrence). */
 int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void* stream);
 
 /* ---- prefix states -------------------------------------------------------
@@ -303,8 +312,9 @@ int replayssm_verify_step(const replayssm_config* cfg, const replayssm_state* st
 
 /* ---- eager comparison kernels -------------------------------------------- */
 
-/* The conventional decode step the method is measured against ("How it
- * works": a conventional step both loads and stores the state): for every
+/* The conventional decode step the method is measured against ("What it
+ * claims": a conventional step loads and also stores the whole state, where
+ * attention only loads its KV cache): for every
  * (sequence, head) load S, S <- alpha S + v k^T (GDN: the gated delta rule),
  * o = S q, store S. S uses the private fp32 layout (replayssm_pack_state).
  *   alpha, beta [B][H]; k, q [B][H][dk]; v [B][H][dv]; out [B][H][dv].
