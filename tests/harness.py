@@ -10,7 +10,24 @@ Error metric, per output vector o (one draft of one head):
     rel = max|o_gpu - o_ref| / max(max|o_ref|, 1e-30)
 and a run reports the maximum over all compared vectors. When whole sequences
 are followed, the same metric is also taken per (sequence, draft) over the
-token's whole layer output (all heads), the vector the bf16-read bar applies to.
+token's whole layer output (all heads).
+
+With a checkpoint copy read in bf16, each head's output is also measured against
+the magnitudes of the terms it sums ("How it works": Standard decoding, the
+output is the decayed checkpoint times q plus the buffered records' sum;
+Two precisions):
+    mag = max|o_gpu - o_ref| / max_p (Gamma_t sum_n |S_ck[p,n] q_t[n]|
+                                      + sum_j gamma_{j,t} |v_j[p]| |k_j . q_t|)
+with S_ck the oracle's checkpoint (its state at position `folded`), j over the
+records since that position up to draft t, and for the delta rule the magnitude
+of each correction's own terms in place of |v_j| (class Magnitudes). The bf16
+rounding of the checkpoint changes each term by at most 2^-8 of its magnitude,
+so this ratio stays bounded where terms cancel and the plain ratio above does
+not. For the fp32 checkpoint the dot products are taken as sum_n |k[n] q[n]|
+(what bounds an fp32 dot product's rounding) and the guarded ratio
+    err / max(max|o_ref|, 1e-2 * mag)
+is the plain metric except on outputs more than 100 times smaller than their
+terms.
 """
 from __future__ import annotations
 
@@ -38,7 +55,19 @@ class Report:
     max_rel_token: float = 0.0  # per (sequence, draft): the layer output over every followed head
     max_rel_u: float = 0.0
     max_rel_ckpt: float = 0.0
+    max_rel_mag: float = 0.0  # per head, against the term magnitudes (when they are formed)
+    mag_vectors: int = 0  # vectors measured against the term magnitudes
+    # per head, err / max(max|o_ref|, 1e-2 * term magnitude): the plain metric unless the output
+    # is more than 100 times smaller than the terms it sums
+    max_rel_guarded: float = 0.0
+    # the vector with the largest plain per-head error: that error, its error against the term
+    # magnitudes, and its cancellation factor (term magnitude / max|o_ref|)
+    worst_rel_vector: Optional[dict] = None
     rels: List[float] = field(default_factory=list)
+    # every compared vector's figures, kept when a drift summary is asked for
+    all_rel: List[np.ndarray] = field(default_factory=list)
+    all_token: List[np.ndarray] = field(default_factory=list)
+    all_mag: List[np.ndarray] = field(default_factory=list)
     pointer_mismatch: int = 0
     ring_mismatch: int = 0
     folds: int = 0
@@ -55,6 +84,104 @@ class Report:
     def update_token(self, r: np.ndarray) -> None:
         if r.size:
             self.max_rel_token = max(self.max_rel_token, float(r.max()))
+
+    def update_mag(self, r: np.ndarray) -> None:
+        if r.size:
+            self.max_rel_mag = max(self.max_rel_mag, float(r.max()))
+            self.mag_vectors += int(r.size)
+
+    def drift_summary(self) -> dict:
+        """Max and 99.9th percentile of every kept figure."""
+        out = {}
+        for name, xs in (("per_head", self.all_rel), ("per_token", self.all_token), ("per_head_magnitude", self.all_mag)):
+            if xs:
+                x = np.concatenate([a.ravel() for a in xs])
+                out[name] = {"max": float(x.max()), "p99_9": float(np.percentile(x, 99.9)), "vectors": int(x.size)}
+        if self.worst_rel_vector is not None:
+            out["worst_per_head_vector"] = self.worst_rel_vector
+        return out
+
+
+class Magnitudes:
+    """Per followed head, the records since its checkpoint position, to form the magnitude
+    denominator of each output: committed records since the last fold, then the drafts.
+
+    Each record keeps U_j, the magnitude of the value vector it carries: |v_j| for Mamba-2;
+    for the delta rule the magnitude of the terms of its correction
+        U_j = beta_j |v_j| + beta_j alpha_j (Gamma_{j-1} sum_n |S_ck[p,n] k_j[n]|
+                                             + sum_{i<j} gamma_{i,j-1} U_i |k_i . k_j|),
+    the bound that |u_j| and its bf16-read error obey (the rebuilt S_{j-1} k_j; "How it
+    works": Gated DeltaNet)."""
+
+    def __init__(self, nh: int, C: int, P: int, N: int, expanded: bool = False):
+        # expanded: every dot product k . x taken as sum_n |k[n] x[n]| (the size of what a
+        # floating-point dot product sums, which bounds its rounding error), else as |k . x|
+        self.expanded = expanded
+        self.n = np.zeros(nh, np.int64)
+        self.a = np.ones((nh, C))
+        self.k = np.zeros((nh, C, N))
+        self.U = np.zeros((nh, C, P))
+
+    def fold(self, folded_heads: np.ndarray) -> None:
+        self.n[folded_heads] = 0
+        self.a[folded_heads] = 1.0
+        self.k[folded_heads] = 0.0
+        self.U[folded_heads] = 0.0
+
+    def _terms(self, Sx, A, K, U, live_end, x):
+        """Magnitude vectors [nh, P] of S_{end} x from the checkpoint and records 0..end, with
+        Sx = sum_n |S_ck[p,n] x[n]| given."""
+        pos = np.arange(A.shape[1])
+        live = pos[None, :] <= live_end[:, None]
+        Ai = np.where(live, A, 1.0)
+        # suffix products: rev[j] = prod of alpha over records j..end; gamma_j = rev[j + 1]
+        rev = np.flip(np.cumprod(np.flip(Ai, axis=1), axis=1), axis=1)
+        gam = np.concatenate([rev[:, 1:], np.ones_like(rev[:, :1])], axis=1)
+        t1 = rev[:, 0][:, None] * Sx
+        if self.expanded:
+            kx = np.matmul(np.abs(K), np.abs(x)[:, :, None])[:, :, 0]
+        else:
+            kx = np.abs(np.matmul(K, x[:, :, None])[:, :, 0])
+        t2 = np.einsum("hj,hjp->hp", np.where(live, gam * kx, 0.0), U)
+        # an empty record set (end = -1) leaves the checkpoint term with Gamma = 1
+        return t1 + t2
+
+    def bounds(self, ckpt, alpha, k, v, q, beta=None):
+        """[nh, T] denominators for drafts with inputs alpha, k, v (raw), beta (delta rule), q;
+        also the drafts' U [nh, T, P] for the accept that follows."""
+        nh, T = q.shape[:2]
+        R = int(self.n.max()) + T
+        A, K, U = self.a[:, :R].copy(), self.k[:, :R].copy(), self.U[:, :R].copy()
+        rows = np.arange(nh)
+        absS = np.abs(ckpt)
+        q = q.astype(np.float64)
+        # sum_n |S_ck[p,n] x[n]| for every draft's q (and k), one batched product each
+        Sq = np.matmul(absS, np.abs(q).transpose(0, 2, 1)).transpose(0, 2, 1)
+        Sk = None if beta is None else np.matmul(absS, np.abs(k.astype(np.float64)).transpose(0, 2, 1)).transpose(0, 2, 1)
+        Ud = np.empty((nh, T, v.shape[-1]))
+        out = np.empty((nh, T))
+        for i in range(T):
+            A[rows, self.n + i] = alpha[:, i]
+            K[rows, self.n + i] = k[:, i]
+            if beta is None:
+                Ud[:, i] = np.abs(v[:, i])
+            else:  # the correction's terms, from the state before draft i (records up to n + i - 1)
+                W = self._terms(Sk[:, i], A, K, U, self.n + i - 1, k[:, i].astype(np.float64))
+                b = np.asarray(beta[:, i], np.float64)[:, None]
+                Ud[:, i] = b * (np.abs(v[:, i]) + np.asarray(alpha[:, i], np.float64)[:, None] * W)
+            U[rows, self.n + i] = Ud[:, i]
+            out[:, i] = self._terms(Sq[:, i], A, K, U, self.n + i, q[:, i]).max(axis=1)
+        return out, Ud
+
+    def commit(self, acc: np.ndarray, alpha, k, U) -> None:
+        rows = np.arange(len(acc))
+        for i in range(int(acc.max()) if acc.size else 0):
+            m = acc > i
+            r = rows[m]
+            self.a[r, self.n[m]] = alpha[m, i]
+            self.k[r, self.n[m]] = k[m, i]
+            self.U[r, self.n[m]] = U[m, i]
+            self.n[m] += 1
 
 
 def whole_sequences(B: int, H: int, seqs: Sequence[int]) -> List[Tuple[int, int]]:
@@ -77,8 +204,10 @@ class Runner:
 
     def __init__(self, shape: LayerShape, L: int, T_max: int, precision: str = "fp32", seed: int = 0,
                  wid: int = 99, heads: Optional[Sequence[Tuple[int, int]]] = None, gen: str = "host",
-                 s0_sigma: float = 0.1, decay: str = "recipe", check_ring: bool = True):
+                 s0_sigma: float = 0.1, decay: str = "recipe", check_ring: bool = True,
+                 keep_all: bool = False, magnitudes: Optional[bool] = None):
         self.shape, self.L, self.T_max, self.seed, self.wid = shape, L, T_max, seed, wid
+        self.keep_all = keep_all
         self.gen, self.decay, self.check_ring = gen, decay, check_ring
         self.cfg = rs.make_config(shape.kind, precision, shape.B, shape.H, shape.P, shape.N, L, T_max)
         self.layer = rs.LayerState(self.cfg)
@@ -98,6 +227,12 @@ class Runner:
         seqs = sorted({b for b, _ in self.heads})
         self.token_groups = (len(self.heads) == len(seqs) * shape.H and
                              self.heads == [(b, h) for b in seqs for h in range(shape.H)])
+        # magnitude bounds of the outputs whenever a bf16 checkpoint copy is read (or when asked)
+        if magnitudes is None:
+            magnitudes = precision != "fp32"
+        self.mag = (Magnitudes(len(self.heads), L + T_max, shape.P, shape.N, expanded=precision == "fp32")
+                    if magnitudes else None)
+        self._mag_pending = None
 
     # -- inputs --------------------------------------------------------------
     def inputs(self, T: int) -> Dict[str, torch.Tensor]:
@@ -135,9 +270,12 @@ class Runner:
         self._slots = slots
         if self.check_ring:
             self._check_ring(x, slots, 1, check_v=beta is None)
-        ref, u, folds = self.oracle.decode(self._sel(x["q"]))
+        pd = self.oracle.pending
+        q = self._sel(x["q"])
+        ref, u, folds = self.oracle.decode(q)
         got = self._sel(out)
-        self._score(got, ref)
+        self._score(got, ref, self._bounds(pd, q, u, folds))
+        self._commit_mag(np.ones(len(self.heads), np.int64))
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
@@ -155,14 +293,32 @@ class Runner:
         self._slots = slots
         if self.check_ring:
             self._check_ring(x, slots, T, check_v=beta is None)
-        ref, u, folds = self.oracle.verify(self._sel(x["q"]))
+        pd = self.oracle.pending
+        q = self._sel(x["q"])
+        ref, u, folds = self.oracle.verify(q)
         got = self._sel(out)
-        self._score(got, ref)
+        self._score(got, ref, self._bounds(pd, q, u, folds))
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
             self._check_u(u, T)
         return got
+
+    # -- magnitude bounds (bf16-read modes) ------------------------------------
+    def _bounds(self, pd, q, u, folds):
+        """Denominators of the drafts' outputs; records the drafts for the accept that follows."""
+        if self.mag is None:
+            return None
+        folded = np.array([folds[b] for b, _ in self.heads], dtype=bool)
+        self.mag.fold(folded)
+        bound, U = self.mag.bounds(self.oracle.ckpt, pd["alpha"], pd["k"], pd["v"], q, pd.get("beta"))
+        self._mag_pending = (pd["alpha"], pd["k"], U)
+        return bound
+
+    def _commit_mag(self, acc_heads: np.ndarray) -> None:
+        if self.mag is not None and self._mag_pending is not None:
+            self.mag.commit(np.asarray(acc_heads, np.int64), *self._mag_pending)
+            self._mag_pending = None
 
     def _check_ring(self, x, slots, T, check_v=True) -> None:
         # committed-record copies are bit-exact copies of the inputs (k and alpha always, v for Mamba-2
@@ -184,31 +340,56 @@ class Runner:
         sh = self.shape
         out = torch.empty((sh.B, 1, sh.H, sh.P), dtype=torch.float32, device="cuda")
         rs.decode(self.cfg, self.layer.struct, x["q"], out)
-        ref, u, folds = self.oracle.decode(self._sel(x["q"]))
+        pd = self.oracle.pending
+        q = self._sel(x["q"])
+        ref, u, folds = self.oracle.decode(q)
         got = self._sel(out)
-        self._score(got, ref)
+        self._score(got, ref, self._bounds(pd, q, u, folds))
+        self._commit_mag(np.ones(len(self.heads), np.int64))
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
             self._check_u(u, 1)
         return got
 
-    def _score(self, got: np.ndarray, ref: np.ndarray) -> None:
-        self.report.update(rel_err(got, ref).ravel())
+    def _score(self, got: np.ndarray, ref: np.ndarray, bound: Optional[np.ndarray] = None) -> None:
+        rel = rel_err(got, ref)
+        self.report.update(rel.ravel())
+        if self.keep_all:
+            self.report.all_rel.append(rel.astype(np.float32))
+        if bound is not None:
+            err = np.abs(got.astype(np.float64) - ref.astype(np.float64)).max(axis=-1)
+            mag = err / np.maximum(bound, 1e-30)
+            self.report.update_mag(mag.ravel())
+            guard = err / np.maximum(np.maximum(np.abs(ref).max(axis=-1), 1e-2 * bound), 1e-30)
+            self.report.max_rel_guarded = max(self.report.max_rel_guarded, float(guard.max()))
+            if self.keep_all:
+                self.report.all_mag.append(mag.astype(np.float32))
+            i = int(np.argmax(rel))
+            w = self.report.worst_rel_vector
+            if rel.size and (w is None or float(rel.flat[i]) > w["rel"]):
+                omax = float(np.abs(ref.reshape(-1, ref.shape[-1])[i]).max())
+                self.report.worst_rel_vector = {"rel": float(rel.flat[i]), "rel_magnitude": float(mag.flat[i]),
+                                                "cancellation": float(bound.flat[i]) / max(omax, 1e-30)}
         if self.token_groups:
             H, P = self.shape.H, self.shape.P
             T = got.shape[1]
             g = got.reshape(-1, H, T, P).transpose(0, 2, 1, 3).reshape(-1, T, H * P)
             r = ref.reshape(-1, H, T, P).transpose(0, 2, 1, 3).reshape(-1, T, H * P)
-            self.report.update_token(rel_err(g, r).ravel())
+            tok = rel_err(g, r)
+            self.report.update_token(tok.ravel())
+            if self.keep_all:
+                self.report.all_token.append(tok.astype(np.float32))
 
     def verify(self, x: Dict[str, torch.Tensor], T: int) -> np.ndarray:
         sh = self.shape
         out = torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda")
         rs.verify(self.cfg, self.layer.struct, T, x["q"], out)
-        ref, u, folds = self.oracle.verify(self._sel(x["q"]))
+        pd = self.oracle.pending
+        q = self._sel(x["q"])
+        ref, u, folds = self.oracle.verify(q)
         got = self._sel(out)
-        self._score(got, ref)
+        self._score(got, ref, self._bounds(pd, q, u, folds))
         self.report.calls += 1
         self.report.folds += sum(folds)
         if u is not None:
@@ -223,11 +404,16 @@ class Runner:
 
     def accept(self, a: torch.Tensor) -> None:
         rs.accept(self.cfg, self.layer.struct, a)
-        self.oracle.accept(a.cpu().numpy())
+        ah = a.cpu().numpy()
+        self.oracle.accept(ah)
+        self._commit_mag(ah[[b for b, _ in self.heads]])
 
     def flush(self) -> None:
         rs.flush(self.cfg, self.layer.struct)
-        self.report.folds += sum(self.oracle.flush())
+        folds = self.oracle.flush()
+        self.report.folds += sum(folds)
+        if self.mag is not None:
+            self.mag.fold(np.array([folds[b] for b, _ in self.heads], dtype=bool))
 
     # -- checks --------------------------------------------------------------
     def check_pointers(self) -> bool:

@@ -113,6 +113,7 @@ def test_mamba2_two_precision_spec():
     assert r.max_alpha_rel <= ALPHA_RTOL
     assert rep.max_rel_ckpt <= 1e-4  # the fp32 checkpoint carries the exact recurrence
     assert rep.max_rel_token <= 2e-2, rep  # token outputs with the bf16 copy read off-fold
+    assert rep.mag_vectors > 0 and rep.max_rel_mag <= 2e-2, rep  # every head, against its terms' magnitudes
 
 
 @pytest.mark.parametrize("precision", ["fp32", "fp32_hp_bf16_lp"])
@@ -125,7 +126,7 @@ def test_gdn_spec(precision):
     if precision == "fp32":
         assert rep.max_rel <= 1e-4 and rep.max_rel_u <= 1e-4, rep
     else:
-        assert rep.max_rel_token <= 2e-2, rep
+        assert rep.max_rel_token <= 2e-2 and rep.mag_vectors > 0 and rep.max_rel_mag <= 2e-2, rep
 
 
 def test_extreme_time_steps():

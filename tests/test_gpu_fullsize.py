@@ -6,6 +6,9 @@ layer. Every step's sampled outputs are compared; the pointer arrays of all
 sequences are compared bit for bit every few steps; the ring copies of the
 sampled heads after every append; the checkpoint at the end.
 """
+import json
+import os
+
 import pytest
 import torch
 
@@ -75,38 +78,70 @@ def test_gdn_b256_verify_T4():
     _clean(rep)
 
 
-def test_mamba2_two_precision_b256_1024_rounds():
-    """T=4, 1024 speculative rounds of the two-precision layer, next to the shared-bf16 comparison.
+def _drift_out(name, data):
+    """Writes a drift summary as JSON when REPLAYSSM_DRIFT_OUT names a directory."""
+    d = os.environ.get("REPLAYSSM_DRIFT_OUT")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, f"{name}.json"), "w") as f:
+            json.dump(data, f, indent=1)
 
-    Two-precision: each token's layer output within 2e-2 of the fp32 oracle (every head of the
-    followed sequences), and the fp32 checkpoint still the exact recurrence (1e-4). Shared bf16:
-    its drift is reported; it must exceed the two-precision drift (its rounding enters the
-    recurrence at every fold) and stay sane."""
+
+def test_mamba2_two_precision_b256_1024_rounds():
+    """T=4, 1024 speculative rounds of the two-precision layer, beside the shared-bf16 and fp32
+    checkpoints on the same inputs ("How it works": Two precisions).
+
+    Every head's output of every draft of three whole sequences is compared with the fp64 oracle:
+    with a bf16 copy read (both bf16 modes) the error stays within 2e-2 of the magnitudes of the
+    terms the output sums, per head; the two-precision token outputs within 2e-2 of the token's
+    size, and its fp32 checkpoint remains the exact recurrence (1e-4); the fp32 mode within 1e-4
+    per head. The shared-bf16 drift must exceed the two-precision drift (its rounding enters the
+    recurrence at every fold)."""
     w = WORKLOADS["mamba2_2prec_b256"]
     sh = w.shape
     heads = whole_sequences(sh.B, sh.H, [0, 97, sh.B - 1])
     drift = {}
-    for precision in ("fp32_hp_bf16_lp", "bf16_shared"):
+    for precision in ("fp32_hp_bf16_lp", "bf16_shared", "fp32"):
         r = Runner(sh, w.L, w.T, precision=precision, wid=w.wid, heads=heads, gen="device",
-                   s0_sigma=w.s0_sigma, check_ring=False)
+                   s0_sigma=w.s0_sigma, check_ring=False, keep_all=True, magnitudes=True)
         rep = run_spec(r, w.T, w.steps, check_every=32)
         assert rep.pointer_mismatch == 0 and rep.err_word == 0
-        drift[precision] = {"token": rep.max_rel_token, "per_head": rep.max_rel, "ckpt": rep.max_rel_ckpt}
-    print("max drift vs the fp32 oracle:", drift)
-    assert drift["fp32_hp_bf16_lp"]["token"] <= TOL_LP, drift
-    assert drift["fp32_hp_bf16_lp"]["ckpt"] <= TOL, drift
-    assert drift["bf16_shared"]["token"] < 0.1, drift
-    assert drift["bf16_shared"]["token"] > drift["fp32_hp_bf16_lp"]["token"], drift
+        assert rep.mag_vectors == len(heads) * w.T * w.steps
+        drift[precision] = {**rep.drift_summary(), "checkpoint_max": rep.max_rel_ckpt, "folds": rep.folds,
+                            "max_per_head_magnitude": rep.max_rel_mag, "max_per_head_guarded": rep.max_rel_guarded}
+    print("drift vs the fp64 oracle:", json.dumps(drift))
+    _drift_out("mamba2_b256_1024_rounds", {"B": sh.B, "rounds": w.steps, "T": w.T, "L": w.L,
+                                           "followed_sequences": [0, 97, sh.B - 1], "modes": drift})
+    two, shared, f32 = drift["fp32_hp_bf16_lp"], drift["bf16_shared"], drift["fp32"]
+    # per head, against the magnitudes of the terms each output sums, in both bf16 modes
+    assert two["max_per_head_magnitude"] <= TOL_LP and shared["max_per_head_magnitude"] <= TOL_LP, drift
+    assert two["per_token"]["max"] <= TOL_LP, drift
+    assert two["checkpoint_max"] <= TOL, drift
+    # fp32: the plain per-head metric, guarded only on outputs 100x smaller than their terms
+    assert f32["max_per_head_guarded"] <= TOL and f32["per_head"]["p99_9"] <= TOL / 10, drift
+    assert f32["checkpoint_max"] <= TOL, drift
+    assert shared["per_token"]["max"] < 0.1, drift
+    assert shared["per_token"]["max"] > two["per_token"]["max"], drift
 
 
 @pytest.mark.parametrize("B", [1, 32, 512])
 def test_two_precision_batch_sweep(B):
+    """The batch sweep of the two-precision layer (1024 rounds each, both bf16 modes): the kernel
+    variant changes with the batch (one or two checkpoint tiles per wavefront), the bound does not."""
     w = WORKLOADS["mamba2_2prec_b256"]
     sh = LayerShape("mamba2", B, 128, 64, 128)
-    r = Runner(sh, w.L, w.T, precision="fp32_hp_bf16_lp", wid=w.wid + B, heads=whole_sequences(B, 128, [0, B - 1]),
-               gen="device", s0_sigma=w.s0_sigma, check_ring=False)
-    rep = run_spec(r, w.T, 64, check_every=8)
-    print(f"B={B}: token drift {rep.max_rel_token:.3e}, per-head max {rep.max_rel:.3e}")
-    assert rep.pointer_mismatch == 0 and rep.err_word == 0
-    assert rep.max_rel_token <= TOL_LP
-    assert rep.max_rel_ckpt <= TOL
+    seqs = [0, B - 1]
+    drift = {}
+    for precision in ("fp32_hp_bf16_lp", "bf16_shared"):
+        r = Runner(sh, w.L, w.T, precision=precision, wid=w.wid + B, heads=whole_sequences(B, 128, seqs),
+                   gen="device", s0_sigma=w.s0_sigma, check_ring=False, keep_all=True)
+        rep = run_spec(r, w.T, w.steps, check_every=64)
+        assert rep.pointer_mismatch == 0 and rep.err_word == 0
+        assert rep.mag_vectors > 0 and rep.max_rel_mag <= TOL_LP, (precision, rep.max_rel_mag)
+        drift[precision] = {**rep.drift_summary(), "checkpoint_max": rep.max_rel_ckpt,
+                            "max_per_head_magnitude": rep.max_rel_mag}
+    print(f"B={B}:", json.dumps(drift))
+    _drift_out(f"mamba2_b{B}_1024_rounds", {"B": B, "rounds": w.steps, "T": w.T, "L": w.L,
+                                            "followed_sequences": sorted(set(seqs)), "modes": drift})
+    assert drift["fp32_hp_bf16_lp"]["per_token"]["max"] <= TOL_LP
+    assert drift["fp32_hp_bf16_lp"]["checkpoint_max"] <= TOL

@@ -33,6 +33,7 @@ def _lp_clean(rep):
     assert rep.pointer_mismatch == 0, (rep.final_pointers, rep.oracle_pointers)
     assert rep.err_word == 0
     assert rep.max_rel_token <= TOL_LP, rep.max_rel_token
+    assert rep.mag_vectors > 0 and rep.max_rel_mag <= TOL_LP, rep.max_rel_mag  # per head, against the terms' magnitudes
     assert rep.max_rel_ckpt <= TOL, rep.max_rel_ckpt
 
 

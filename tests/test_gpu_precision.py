@@ -72,6 +72,8 @@ def test_two_precision_drifts_less_than_shared_bf16():
         rep = run_spec(r, 4, 160, check_every=40)
         assert rep.pointer_mismatch == 0 and rep.err_word == 0
         drift[prec] = rep.max_rel_token
+        if prec == "fp32_hp_bf16_lp":  # per head, against the magnitudes of the terms it sums
+            assert rep.mag_vectors > 0 and rep.max_rel_mag <= 2e-2, rep.max_rel_mag
     assert drift["fp32"] <= 1e-4
     assert drift["fp32_hp_bf16_lp"] <= 2e-2
     assert drift["fp32_hp_bf16_lp"] < drift["bf16_shared"], drift
