@@ -29,12 +29,16 @@ distinct steps, cycled when K + W exceeds it). Prints one JSON line:
              with --sweep the two-precision batch sweep B in {1, 32, 256, 512},
              each warm (one layer) and rotated (rounds cycle over layer instances
              holding >= 2 GiB of state, so the on-package cache cannot hold it)
+  drift      output drift of the bf16-read checkpoints (two-precision and shared bf16) against
+             an fp32-checkpoint layer on the same inputs: 1024 T=4 rounds at B=256, and the
+             batch sweep B in {1, 32, 512}; per-head and per-token max and 99.9th percentile
   window_sweep  with --window-sweep: L in {4..64} x T in {1, 4, 8} at the headline shape
   ceilings   practical HBM ceilings measured on the device: a read-only probe in
              the checkpoint stream's access pattern, and a device-to-device copy
-  cpu_baseline  the CPU oracle (fp64 eager recurrence, OpenMP over heads) on a
-             bounded sample of the same workload, scaled to tokens/s; also on one
-             core and on the Gated DeltaNet workload
+  cpu_baseline  the CPU oracle (fp32 eager recurrence, OpenMP over heads) on the
+             headline workload at full shape, all cores: up to 32 timed decode steps on
+             their own inputs; also on one core, in fp64, and on the Gated DeltaNet and
+             KDA workloads
 """
 from __future__ import annotations
 
@@ -91,7 +95,8 @@ def parse():
     ap.add_argument("--workload", default="mamba2_decode_b256")
     ap.add_argument("--quick", action="store_true", help="headline workload only (no extras, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="cap on the timed oracle seconds of each CPU-baseline figure")
     ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
     ap.add_argument("--window-sweep", action="store_true", help="also run the window-size sweep L x T")
     ap.add_argument("--leg", choices=sorted(LEGS),
@@ -267,6 +272,20 @@ def run_standard_decode(torch, rs, synth, w, steps, warmup, seed, kernel_pass=Tr
             by_h.setdefault(hh, []).append(durs[i] * 1e3)
             hh = 1 if hh + 1 > w.L else hh + 1
         res["us_by_h"] = {int(k): round(float(np.mean(v)), 1) for k, v in sorted(by_h.items())}
+        # Steady state: the timed window's decode launches replaced by one whole L-step cycle's
+        # (h = 1..L before the step; the append's cost does not depend on h). Both figures come
+        # from the same event-timed launches, so their event overhead cancels.
+        t_of_h = {k: float(np.mean(v)) for k, v in by_h.items()}
+        cycle = list(range(1, w.L + 1))
+        if all(hh in t_of_h for hh in cycle):
+            hh, timed = h0, []
+            for _ in range(steps):
+                timed.append(t_of_h.get(hh, np.nan))
+                hh = 1 if hh + 1 > w.L else hh + 1
+            if not np.isnan(timed).any():
+                ms_step = tm.ms / steps - np.mean(timed) * 1e-3 + np.mean([t_of_h[c] for c in cycle]) * 1e-3
+                res["steady_ms_per_step"] = ms_step
+                res["steady_tokens_per_s"] = sh.B / (ms_step * 1e-3)
         res.update({"kernel_ms_total": float(durs.sum()), "kernel_launches": steps, "kernel_bytes": kb,
                     "kernel_avg_us": float(durs.mean() * 1e3),
                     "fold_avg_us": float(np.mean(fold_ms) * 1e3) if fold_ms else None,
@@ -364,6 +383,61 @@ def run_spec(torch, rs, synth, w, rounds, warmup, seed, precision=None, B=None, 
         err = rs.read_error(lay.struct)
         if err:
             raise RuntimeError(f"device error word {err}")
+    return res
+
+
+def run_drift(torch, rs, synth, w, B, rounds, seed):
+    """Output drift of the two bf16-read checkpoints over `rounds` speculative rounds (fused append +
+    verify of T drafts, accepted prefix ~ U{0..T}): the two-precision layer (bf16 copy read off-fold)
+    and the shared-bf16 layer run beside an fp32-checkpoint layer on identical inputs, and every
+    draft output of every sequence and head is compared with the fp32 layer's (which the parity
+    tests hold within 1e-4 of the fp64 oracle per head). Per head: max|o - o_fp32| / max|o_fp32|
+    over the head's output vector; per token: the same over the token's whole layer output (all
+    heads). Reported: max and 99.9th percentile over all vectors."""
+    sh = synth.LayerShape(w.shape.kind, B, w.shape.H, w.shape.P, w.shape.N)
+    T = w.T
+    modes = ("fp32", "fp32_hp_bf16_lp", "bf16_shared")
+    S0 = synth.device_initial_state(seed, w.wid, sh, w.s0_sigma, "cuda")
+    cfgs = {m: rs.make_config(sh.kind, m, sh.B, sh.H, sh.P, sh.N, w.L, T) for m in modes}
+    lays = {m: rs.LayerState(cfgs[m]) for m in modes}
+    for m in modes:
+        lays[m].import_state(S0)
+    del S0
+    outs = {m: torch.empty((sh.B, T, sh.H, sh.P), dtype=torch.float32, device="cuda") for m in modes}
+    head = {m: torch.empty((rounds, sh.B, T, sh.H), dtype=torch.float32, device="cuda") for m in modes[1:]}
+    tok = {m: torch.empty((rounds, sh.B, T), dtype=torch.float32, device="cuda") for m in modes[1:]}
+    wid = w.wid + 7000
+    for r in range(rounds):
+        x = synth.device_step(seed, wid, r, sh, T, "cuda")
+        acc = synth.device_accept(seed, wid, r, sh.B, T, "cuda")
+        for m in modes:
+            st = lays[m].struct
+            rs.verify_step(cfgs[m], st, T, x["alpha"], x["k"], x["v"], x.get("beta"), x["q"], outs[m])
+            rs.accept(cfgs[m], st, acc)
+        ref = outs["fp32"]
+        den_h = ref.abs().amax(-1).clamp_min(1e-30)
+        den_t = ref.abs().amax((2, 3)).clamp_min(1e-30)
+        for m in modes[1:]:
+            d = (outs[m] - ref).abs()
+            head[m][r] = d.amax(-1) / den_h
+            tok[m][r] = d.amax((2, 3)) / den_t
+    torch.cuda.synchronize()
+    for m in modes:
+        err = rs.read_error(lays[m].struct)
+        if err:
+            raise RuntimeError(f"device error word {err} ({m})")
+
+    def stats(x):
+        x = x.flatten()
+        k = max(1, x.numel() // 1000)
+        return {"max": float(x.max().item()), "p99_9": float(torch.topk(x, k).values.min().item()),
+                "vectors": int(x.numel())}
+
+    res = {"B": B, "rounds": rounds, "T": T, "L": w.L, "reference": "fp32-checkpoint layer on the same inputs"}
+    for m in modes[1:]:
+        res[m] = {"per_head": stats(head[m]), "per_token": stats(tok[m])}
+    del lays, outs, head, tok
+    torch.cuda.empty_cache()
     return res
 
 
@@ -624,48 +698,57 @@ def host_cpu():
     return {"model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(synth, w, seed, seconds, threads=None, seqs=64):
-    """The oracle as it stands, on a bounded sample of the workload: `seqs` sequences (all heads),
-    as many of the workload's 512 steps as fit in about `seconds` of oracle time."""
+_CPU_INPUTS = {}
+
+
+def cpu_baseline(synth, w, seed, seconds, threads=None, precision="f32", max_steps=32, warmup=2):
+    """The oracle as it stands (the eager recurrence, OpenMP over heads) at the workload's full
+    shape: every sequence and head, `warmup` untimed steps, then up to `max_steps` timed decode
+    steps (fewer if `seconds` of oracle time run out first), each on its own seeded inputs, whose
+    generation is not timed."""
     import oracle
 
     if threads is not None:
         prev = oracle.num_threads()
         oracle.set_num_threads(threads)
         try:
-            return cpu_baseline(synth, w, seed, seconds, seqs=seqs)
+            return cpu_baseline(synth, w, seed, seconds, precision=precision, max_steps=max_steps, warmup=warmup)
         finally:
             oracle.set_num_threads(prev)
 
     sh = w.shape
-    Bs = min(seqs, sh.B)
-    sub = synth.LayerShape(sh.kind, Bs, sh.H, sh.P, sh.N)
-    nh = Bs * sh.H
-    S = synth.host_initial_state(seed, w.wid, sub, w.s0_sigma).reshape(nh, sh.P, sh.N).astype(np.float64)
+    nh = sh.B * sh.H
+    dt = np.float64 if precision == "f64" else np.float32
+    S = synth.host_initial_state(seed, w.wid, sh, w.s0_sigma).reshape(nh, sh.P, sh.N).astype(dt)
     acc = np.ones(nh, np.int32)
-    # a few distinct steps of inputs, reused cyclically (the oracle's work does not depend on values)
-    inputs = []
-    for t in range(4):
-        x = synth.host_step(seed, w.wid, t, sub, 1)
-        inputs.append({k: np.ascontiguousarray(np.swapaxes(v, 1, 2)).reshape(nh, 1, *v.shape[3:])
-                       for k, v in x.items()})
     steps, spent = 0, 0.0
-    while spent < seconds and steps < 512:
-        args = inputs[steps % len(inputs)]
+    for t in range(warmup + max_steps):
+        key = (w.name, seed, t)
+        if key not in _CPU_INPUTS:  # generated once per step and shared by the runs (not timed)
+            x = synth.host_step(seed, w.wid, t, sh, 1)
+            _CPU_INPUTS[key] = {k: np.ascontiguousarray(np.swapaxes(v, 1, 2)).reshape(nh, 1, *v.shape[3:])
+                                for k, v in x.items()}
+        args = _CPU_INPUTS[key]
         t0 = time.perf_counter()
         if sh.kind == "mamba2":
-            oracle.mamba2_round(S, args["alpha"].reshape(nh, 1), args["k"], args["v"], args["q"], acc)
+            oracle.mamba2_round(S, args["alpha"].reshape(nh, 1), args["k"], args["v"], args["q"], acc, precision)
         elif sh.kind == "kda":
-            oracle.kda_round(S, args["alpha"], args["beta"].reshape(nh, 1), args["k"], args["v"], args["q"], acc)
+            oracle.kda_round(S, args["alpha"], args["beta"].reshape(nh, 1), args["k"], args["v"], args["q"], acc,
+                             precision)
         else:
             oracle.gdn_round(S, args["alpha"].reshape(nh, 1), args["beta"].reshape(nh, 1), args["k"], args["v"],
-                             args["q"], acc)
-        spent += time.perf_counter() - t0
-        steps += 1
-    return {"value": Bs * steps / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+                             args["q"], acc, precision)
+        if t >= warmup:
+            spent += time.perf_counter() - t0
+            steps += 1
+            if spent >= seconds:
+                break
+    name = {"f32": "fp32", "f64": "fp64"}[precision]
+    return {"value": sh.B * steps / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "host": host_cpu(),
-            "sample": f"{Bs} of {sh.B} sequences (all {sh.H} heads), {steps} decode steps, fp64 eager "
-                      f"recurrence, {spent:.1f} s of oracle time (input generation excluded)"}
+            "sample": f"{w.name} at full shape ({sh.B} sequences x {sh.H} heads, {sh.P}x{sh.N} state), "
+                      f"{steps} decode steps after {warmup} warm-up steps, {name} eager recurrence, "
+                      f"{spent:.1f} s of oracle time (input generation excluded)"}
 
 
 # Single legs (--leg NAME), each on its own workload: K steps or rounds after W warm-up ones.
@@ -696,6 +779,8 @@ LEGS = {
     "conv_decode": lambda torch, rs, synth, k, w, seed: run_conv(torch, rs, synth, 256, 40960, 4, 1, k, w, seed),
     "kda_spec": lambda torch, rs, synth, k, w, seed: run_spec(
         torch, rs, synth, synth.WORKLOADS["kda_decode_b256"], k, w, seed),
+    "drift": lambda torch, rs, synth, k, w, seed: {f"B{B}": run_drift(
+        torch, rs, synth, synth.WORKLOADS["mamba2_2prec_b256"], B, k, seed) for B in (256, 1, 32, 512)},
 }
 
 
@@ -754,27 +839,37 @@ def main():
                          "flops_per_fold_step": fold_flops}},
         "step_gbs": (main_res["decode_bytes"] + main_res["append_bytes"]) / (main_res["ms"] * 1e6),
         "step": "replayssm_append then replayssm_decode",
+        "steady_state_tokens_per_s": main_res.get("steady_tokens_per_s"),
+        "steady_state_ms_per_step": main_res.get("steady_ms_per_step"),
+        "steady_state": "the timed K steps with their decode launches replaced by one whole window of "
+                        "L steps (h = 1..L before the step, one fold), from the per-h launch times in "
+                        "us_by_h_before_step; value itself is the K steps as timed",
     }
+    # the other standard-decoding legs time whole windows: a multiple of L steps after a warm-up of
+    # L + 1 steps (one fold), so every timed window holds exactly one fold per L steps
+    sec_steps = max(w.L, (min(args.steps, 256) // w.L) * w.L)
+    sec_warm = w.L + 1
     if not args.quick:
-        fu = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=True)
+        fu = run_standard_decode(torch, rs, synth, w, sec_steps, sec_warm, args.seed, fused=True)
         line["fused"] = {"tokens_per_s": fu["tokens"] / (fu["ms"] * 1e-3),
                          "kernel_gbs": fu["kernel_bytes"] / (fu["kernel_ms_total"] * 1e6),
-                         "kernel_avg_us": fu["kernel_avg_us"],
+                         "kernel_avg_us": fu["kernel_avg_us"], "steps": fu["steps"],
+                         "unfused_steady_state_tokens_per_s": main_res.get("steady_tokens_per_s"),
                          "step": "replayssm_decode_step (append + decode in one launch)"}
     if not args.quick:
-        tp = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False,
+        tp = run_standard_decode(torch, rs, synth, w, sec_steps, sec_warm, args.seed, fused=False,
                                  precision="fp32_hp_bf16_lp")
         line["two_precision"] = {"tokens_per_s": tp["tokens"] / (tp["ms"] * 1e-3),
                                  "kernel_gbs": tp["kernel_bytes"] / (tp["kernel_ms_total"] * 1e6),
                                  "kernel_avg_us": tp["kernel_avg_us"], "plain_step_us": tp["plain_avg_us"],
-                                 "fold_step_us": tp["fold_avg_us"],
+                                 "fold_step_us": tp["fold_avg_us"], "steps": tp["steps"],
                                  "step": "replayssm_append then replayssm_decode, bf16 copy read off-fold"}
     if not args.quick:
-        dtl = run_standard_decode(torch, rs, synth, w, min(args.steps, 256), 16, args.seed, fused=False,
+        dtl = run_standard_decode(torch, rs, synth, w, sec_steps, sec_warm, args.seed, fused=False,
                                   kernel_pass=False, from_dt=True)
         line["decode_from_dt"] = {"tokens_per_s": dtl["tokens"] / (dtl["ms"] * 1e-3),
-                                  "ms_per_step": dtl["ms"] / dtl["steps"],
-                                  "headline_ms_per_step": main_res["ms"] / args.steps,
+                                  "ms_per_step": dtl["ms"] / dtl["steps"], "steps": dtl["steps"],
+                                  "headline_steady_state_ms_per_step": main_res.get("steady_ms_per_step"),
                                   "step": "replayssm_append_dt (decay from the raw time step) then replayssm_decode"}
     if not args.quick:
         eg = run_eager(torch, rs, synth, w, min(args.steps, 256), 16, args.seed)
@@ -834,6 +929,7 @@ def main():
                         "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"]}
         r4["small_batch_graph"] = {f"B{B}": run_spec_graph(torch, rs, synth, w4, B, 16, 20, args.seed)
                                    for B in (1, 32)}
+        line["drift"] = {f"B{B}": run_drift(torch, rs, synth, w4, B, w4.steps, args.seed) for B in (256, 1, 32, 512)}
         if args.sweep:
             sweep = {}
             for B in (1, 32, 256, 512):
@@ -850,15 +946,18 @@ def main():
     if args.window_sweep:
         line["window_sweep"] = window_sweep(torch, rs, synth, args.seed)
     if not (args.quick or args.no_cpu_baseline):
-        line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds, seqs=sh.B)
+        line["cpu_baseline"] = cpu_baseline(synth, w, args.seed, args.cpu_seconds)
         if not args.quick:
-            one = cpu_baseline(synth, w, args.seed, args.cpu_seconds / 2, threads=1)
+            one = cpu_baseline(synth, w, args.seed, args.cpu_seconds, threads=1)
+            f64 = cpu_baseline(synth, w, args.seed, args.cpu_seconds, precision="f64")
             g = synth.WORKLOADS["gdn_decode_b256"]
-            gd = cpu_baseline(synth, g, args.seed, args.cpu_seconds / 2)
+            gd = cpu_baseline(synth, g, args.seed, args.cpu_seconds)
             kd = synth.WORKLOADS["kda_decode_b256"]
-            kc = cpu_baseline(synth, kd, args.seed, args.cpu_seconds / 2)
+            kc = cpu_baseline(synth, kd, args.seed, args.cpu_seconds)
+            _CPU_INPUTS.clear()
             line["cpu_baseline"]["more"] = {
                 "one_core": {"value": one["value"], "cores": one["cores"], "sample": one["sample"]},
+                "fp64": {"value": f64["value"], "cores": f64["cores"], "sample": f64["sample"]},
                 g.name: {"value": gd["value"], "cores": gd["cores"], "sample": gd["sample"]},
                 kd.name: {"value": kc["value"], "cores": kc["cores"], "sample": kc["sample"]}}
     print(json.dumps(line), flush=True)
