@@ -217,6 +217,23 @@ int replayssm_append_dt(const replayssm_config* cfg, const replayssm_state* st, 
                         const float* dt, const float* A, const float* dt_bias, const float* k,
                         const float* v, const float* beta, void* stream);
 
+/* replayssm_append for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation): the
+ * same call, except that the per-sequence arrival counters the append kernel
+ * uses are taken from an array the library holds in device memory
+ * (REPLAYSSM_STATIC_SCRATCH_SEQS int32 counters, 64 KiB, one copy per GPU for
+ * the life of the process, its address looked up on the first call on each
+ * device) instead of st->arrive, which may be NULL. Allocates nothing; each call
+ * clears the counters it uses before the append. B above
+ * REPLAYSSM_STATIC_SCRATCH_SEQS returns REPLAYSSM_EINVAL. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on different
+ * streams without ordering) race on it and must not be issued; stream-ordered
+ * calls are safe. Results are bit-identical to replayssm_append. */
+#define REPLAYSSM_STATIC_SCRATCH_SEQS 16384
+int replayssm_append_static(const replayssm_config* cfg, const replayssm_state* st, int T,
+                            const float* alpha, const float* k, const float* v, const float* beta,
+                            void* stream);
+
 /* One standard decoding step: the single pending record (appended by
  * replayssm_append with T = 1) is the new token t.
  *   - if h + 1 > L, the h committed records are first folded into the

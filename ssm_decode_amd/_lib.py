@@ -75,6 +75,8 @@ SIGNATURES = {
     "replayssm_unpack_state": [ctypes.POINTER(Config), _vp, _vp, _vp, _vp],
     "replayssm_read_error": [ctypes.POINTER(State), ctypes.POINTER(_i32), _vp],
     "replayssm_append": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp],
+    "replayssm_append_static": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp,
+                                _vp],
     "replayssm_append_dt": [ctypes.POINTER(Config), ctypes.POINTER(State), ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp],
     "replayssm_decode": [ctypes.POINTER(Config), ctypes.POINTER(State), _vp, _vp, _vp],
@@ -195,6 +197,11 @@ def read_error(st, stream=None) -> int:
 def append(cfg, st, T, alpha, k, v, beta=None, stream=None):
     _check(lib().replayssm_append(ctypes.byref(cfg), ctypes.byref(st), int(T), _f32(alpha), _f32(k),
                                   _f32(v), _f32(beta), _s(stream)), "append")
+
+
+def append_static(cfg, st, T, alpha, k, v, beta=None, stream=None):
+    _check(lib().replayssm_append_static(ctypes.byref(cfg), ctypes.byref(st), int(T), _f32(alpha), _f32(k),
+                                         _f32(v), _f32(beta), _s(stream)), "append_static")
 
 
 def append_dt(cfg, st, T, dt, A, dt_bias, k, v, beta=None, stream=None):

@@ -89,7 +89,7 @@ int check_config(const replayssm_config* c) {
   return REPLAYSSM_OK;
 }
 
-int check_state(const replayssm_config* c, const replayssm_state* s) {
+int check_state(const replayssm_config* c, const replayssm_state* s, bool need_arrive = true) {
   if (s == nullptr) return fail(REPLAYSSM_EINVAL, "state is NULL");
   if (c->precision != REPLAYSSM_BF16_SHARED) NEED(s->hp);
   if (c->precision != REPLAYSSM_FP32) NEED(s->lp);
@@ -102,7 +102,7 @@ int check_state(const replayssm_config* c, const replayssm_state* s) {
   NEED(s->h);
   NEED(s->p);
   NEED(s->folded);
-  NEED(s->arrive);
+  if (need_arrive) NEED(s->arrive);
   NEED(s->err);
   return REPLAYSSM_OK;
 }
@@ -230,7 +230,7 @@ int replayssm_read_error(const replayssm_state* st, int32_t* err_out, void* stre
 
 static int append_common(const replayssm_config* cfg, const replayssm_state* st, int T, const float* alpha,
                          const float* dt, const float* A, const float* dt_bias, const float* k, const float* v,
-                         const float* beta, void* stream) {
+                         const float* beta, void* stream, bool static_scratch = false) {
   NEED(k);
   NEED(v);
   if (cfg->kind != REPLAYSSM_MAMBA2) NEED(beta);
@@ -261,7 +261,24 @@ static int append_common(const replayssm_config* cfg, const replayssm_state* st,
   a.T_max = cfg->T_max;
   // float4 units per sequence: k rows, KDA gate rows, v rows
   a.units_per_seq = T * cfg->H * ((cfg->kind == REPLAYSSM_KDA ? 2 : 1) * cfg->dk + cfg->dv) / 4;
+  if (static_scratch) {
+    a.arrive = nullptr;
+    return hip_result(rs::launch_append_static(cfg->kind, a, as_stream(stream)), "append_static");
+  }
   return hip_result(rs::launch_append(cfg->kind, a, as_stream(stream)), dt ? "append_dt" : "append");
+}
+
+int replayssm_append_static(const replayssm_config* cfg, const replayssm_state* st, int T,
+                            const float* alpha, const float* k, const float* v, const float* beta,
+                            void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_state(cfg, st, /*need_arrive=*/false)) return r;
+  if (cfg->B > REPLAYSSM_STATIC_SCRATCH_SEQS)
+    return fail(REPLAYSSM_EINVAL, "B=%d above the %d sequences of the library's scratch counters", cfg->B,
+                REPLAYSSM_STATIC_SCRATCH_SEQS);
+  if (T < 1 || T > cfg->T_max) return fail(REPLAYSSM_EINVAL, "T=%d outside 1..T_max=%d", T, cfg->T_max);
+  NEED(alpha);
+  return append_common(cfg, st, T, alpha, nullptr, nullptr, nullptr, k, v, beta, stream, true);
 }
 
 int replayssm_append(const replayssm_config* cfg, const replayssm_state* st, int T,

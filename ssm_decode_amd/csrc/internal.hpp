@@ -160,6 +160,10 @@ int get_tiling();
 // Compute units of the current device (cached per device).
 hipError_t device_cus(int* cus);
 hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s);
+// The same with the per-sequence arrival counters in the library's static device array
+// (a.arrive is ignored; B <= kStaticScratchSeqs): clears them, then appends.
+constexpr int kStaticScratchSeqs = REPLAYSSM_STATIC_SCRATCH_SEQS;
+hipError_t launch_append_static(int kind, const AppendArgs& a, hipStream_t s);
 hipError_t launch_accept(int32_t* h, int32_t* p, int32_t* err, const int32_t* acc, int B, int L,
                          hipStream_t s);
 hipError_t launch_init(int32_t* head, int32_t* h, int32_t* p, int64_t* folded, int32_t* arrive,

@@ -135,6 +135,58 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
   }
 }
 
+// ---- replayssm_append_static: the append without the caller's scratch -------------
+// The append's per-sequence arrival counters live in this array instead of
+// state->arrive, for callers that cannot allocate. Each GPU the library runs on
+// holds its own copy (zero at load) until the process ends. In host code the
+// name is only a stand-in: the device address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) int32_t scratch[kStaticScratchSeqs];
+
+// Device address of `scratch` on the current device.
+static hipError_t static_scratch(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Zeroes n counters (a kernel, not a memset, so that the call can be captured in
+// a graph and replayed).
+__global__ void __launch_bounds__(256) clear_counters_kernel(int32_t* c, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+
+hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s);
+
+hipError_t launch_append_static(int kind, const AppendArgs& args, hipStream_t s) {
+  if (args.B > kStaticScratchSeqs) return hipErrorInvalidValue;  // (the entry point rejects it first)
+  int32_t* counters = nullptr;
+  hipError_t e = static_scratch(&counters);
+  if (e != hipSuccess) return e;
+  // the array keeps what the last call on this device left there: this call's counters start at zero
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((args.B + 255) / 256)), dim3(256), 0, s, counters,
+                     args.B);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AppendArgs a = args;
+  a.arrive = counters;
+  return launch_append(kind, a, s);
+}
+
 hipError_t launch_append(int kind, const AppendArgs& a, hipStream_t s) {
   const int per_block = 256 * 4;
   int chunks = (a.units_per_seq + per_block - 1) / per_block;

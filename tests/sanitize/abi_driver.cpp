@@ -21,6 +21,7 @@ static hipError_t count() {
 hipError_t persistent_grid(const void*, int, size_t, int, int* grid) { *grid = 1; return count(); }
 hipError_t launch_replay(int, int, int, const ReplayArgs&, hipStream_t) { return count(); }
 hipError_t launch_append(int, const AppendArgs&, hipStream_t) { return count(); }
+hipError_t launch_append_static(int, const AppendArgs& a, hipStream_t) { return a.arrive ? hipErrorInvalidValue : count(); }
 hipError_t launch_accept(int32_t*, int32_t*, int32_t*, const int32_t*, int, int, hipStream_t) { return count(); }
 hipError_t launch_init(int32_t*, int32_t*, int32_t*, int64_t*, int32_t*, int32_t*, int, hipStream_t) { return count(); }
 hipError_t launch_pack(const float*, float*, uint16_t*, int64_t, int, int, hipStream_t) { return count(); }
@@ -88,6 +89,15 @@ static void every_call(const replayssm_config& c) {
              REPLAYSSM_OK);
   }
   EXPECT(replayssm_append(&c, &s, c.T_max + 1, F(21), F(22), F(23), beta, nullptr), REPLAYSSM_EINVAL);
+  {
+    // the variant without the caller's scratch: arrive may be NULL, B is capped
+    replayssm_state s0 = s;
+    s0.arrive = nullptr;
+    EXPECT(replayssm_append_static(&c, &s0, 1, F(21), F(22), F(23), beta, nullptr),
+           c.B <= REPLAYSSM_STATIC_SCRATCH_SEQS ? REPLAYSSM_OK : REPLAYSSM_EINVAL);
+    EXPECT(replayssm_append_static(&c, &s0, c.T_max + 1, F(21), F(22), F(23), beta, nullptr), REPLAYSSM_EINVAL);
+    EXPECT(replayssm_append(&c, &s0, 1, F(21), F(22), F(23), beta, nullptr), REPLAYSSM_EINVAL);
+  }
   EXPECT(replayssm_append_dt(&c, &s, 1, F(28), F(29), nullptr, F(22), F(23), beta, nullptr),
          c.kind == REPLAYSSM_KDA ? REPLAYSSM_ENOTSUP : REPLAYSSM_OK);
   EXPECT(replayssm_decode(&c, &s, F(24), F(25), nullptr), REPLAYSSM_OK);
@@ -122,6 +132,11 @@ int main() {
             const replayssm_config c{kind, prec, 3, 5, d[0], d[1], L, T};
             if (replayssm_get_sizes(&c, &sz) == REPLAYSSM_OK) every_call(c);
           }
+  // the static-scratch append at and just past its sequence limit
+  for (int B : {REPLAYSSM_STATIC_SCRATCH_SEQS, REPLAYSSM_STATIC_SCRATCH_SEQS + 1}) {
+    const replayssm_config c{REPLAYSSM_MAMBA2, REPLAYSSM_FP32, B, 2, 64, 128, 16, 4};
+    every_call(c);
+  }
   const replayssm_config huge{REPLAYSSM_MAMBA2, REPLAYSSM_FP32, 65535, 16385, 64, 128, 16, 1};
   EXPECT(replayssm_get_sizes(&huge, &sz), REPLAYSSM_EINVAL);
   const replayssm_config wide{REPLAYSSM_MAMBA2, REPLAYSSM_FP32, 1, 1 << 21, 64, 128, 16, 1};

@@ -214,3 +214,19 @@ def test_binding_constants_match_the_header(rs):
     for name in mirrored:
         assert getattr(rs, name) == defined[name], name
     assert {"TILES_AUTO", "TILES_ONE", "TILES_TWO", "DEVERR_INDEX"} <= set(defined)
+
+
+def test_static_append_rejects_more_sequences_than_its_scratch(rs):
+    """replayssm_append_static holds REPLAYSSM_STATIC_SCRATCH_SEQS counters: one sequence more is
+    refused on the host, before anything would reach a device (no GPU needed), while st->arrive
+    may be NULL."""
+    limit = int(re.search(r"#define REPLAYSSM_STATIC_SCRATCH_SEQS (\d+)", open(HEADER).read()).group(1))
+    assert limit == 16384
+    fake = 1 << 20  # an aligned address that is never dereferenced
+    for B, want in ((limit + 1, rs.EINVAL),):
+        cfg = rs.make_config("mamba2", "fp32", B, 1, 16, 16, 4, 1)
+        st = rs.State(*([fake] * len(rs.State._fields_)))
+        st.lp = st.ring_beta = st.ring_vraw = st.arrive = None
+        status = rs.lib().replayssm_append_static(ctypes.byref(cfg), ctypes.byref(st), 1, fake, fake, fake, None, None)
+        assert status == want
+        assert str(limit).encode() in rs.lib().replayssm_last_error()
