@@ -628,9 +628,6 @@ def window_sweep(torch, rs, synth, seed):
             if T > L:
                 continue
             key = f"L{L}_T{T}"
-            if L + T > 64 + 4:  # L = 64 with T = 8 exceeds the LDS budget (ENOTSUP)
-                cells[key] = "not supported (LDS budget)"
-                continue
             w = dataclasses.replace(base, L=L, T=T, wid=base.wid + 1000 + 10 * L + T)
             if T == 1:
                 r = run_standard_decode(torch, rs, synth, w, max(128, 2 * L), 16, seed, fused=False)

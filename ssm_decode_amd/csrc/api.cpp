@@ -32,8 +32,18 @@ int hip_result(hipError_t e, const char* what) {
   return fail(REPLAYSSM_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-hipError_t replay(const replayssm_config* cfg, int tmax, const rs::ReplayArgs& a, hipStream_t s) {
-  return rs::launch_replay(cfg->kind, cfg->dk, tmax, a, s);
+bool exact_u(const replayssm_config* c);
+
+// Launches the replay kernel after checking its LDS carve against what the current device
+// gives one workgroup (ENOTSUP beyond it).
+int replay(const replayssm_config* cfg, int tmax, const rs::ReplayArgs& a, hipStream_t s, const char* what) {
+  const rs::ReplayLds lds(cfg->L + cfg->T_max, cfg->dk, cfg->dv, tmax, exact_u(cfg) ? rs::kKindGdnExact : cfg->kind);
+  int max_lds = 0;
+  if (int r = hip_result(rs::device_max_lds(&max_lds), what)) return r;
+  if (lds.total * 4 > max_lds)
+    return fail(REPLAYSSM_ENOTSUP, "%s: L + T_max and dims need %d bytes of LDS; the device gives a workgroup %d",
+                what, lds.total * 4, max_lds);
+  return hip_result(rs::launch_replay(cfg->kind, cfg->dk, tmax, a, s), what);
 }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -83,9 +93,9 @@ int check_config(const replayssm_config* c) {
                 "FP32_HP_BF16_LP)");
   const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max),
                           exact_u(c) ? rs::kKindGdnExact : c->kind);
-  if (lds.total * 4 > rs::kMaxLdsBytes)
-    return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d)", lds.total * 4,
-                rs::kMaxLdsBytes);
+  if (lds.total * 4 > rs::kArchMaxLdsBytes)
+    return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d on gfx950)", lds.total * 4,
+                rs::kArchMaxLdsBytes);
   return REPLAYSSM_OK;
 }
 
@@ -311,7 +321,7 @@ int replayssm_decode(const replayssm_config* cfg, const replayssm_state* st, con
   NEED(q);
   NEED(out);
   const rs::ReplayArgs a = replay_args(cfg, st, 1, rs::kModeDecode, q, out);
-  return hip_result(replay(cfg, 1, a, as_stream(stream)), "decode");
+  return replay(cfg, 1, a, as_stream(stream), "decode");
 }
 
 int replayssm_verify(const replayssm_config* cfg, const replayssm_state* st, int T, const float* q,
@@ -322,8 +332,7 @@ int replayssm_verify(const replayssm_config* cfg, const replayssm_state* st, int
   NEED(q);
   NEED(out);
   const rs::ReplayArgs a = replay_args(cfg, st, T, rs::kModeVerify, q, out);
-  return hip_result(replay(cfg, tmax_bucket(T), a, as_stream(stream)),
-                    "verify");
+  return replay(cfg, tmax_bucket(T), a, as_stream(stream), "verify");
 }
 
 static int fused_call(const replayssm_config* cfg, const replayssm_state* st, int T, int mode,
@@ -344,7 +353,7 @@ static int fused_call(const replayssm_config* cfg, const replayssm_state* st, in
   a.in_k = k;
   a.in_v = v;
   a.fused = 1;
-  return hip_result(replay(cfg, tmax_bucket(T), a, as_stream(stream)), what);
+  return replay(cfg, tmax_bucket(T), a, as_stream(stream), what);
 }
 
 int replayssm_decode_step(const replayssm_config* cfg, const replayssm_state* st, const float* alpha,
@@ -373,7 +382,7 @@ int replayssm_flush(const replayssm_config* cfg, const replayssm_state* st, void
   if (int r = check_config(cfg)) return r;
   if (int r = check_state(cfg, st)) return r;
   const rs::ReplayArgs a = replay_args(cfg, st, 0, rs::kModeFlush, nullptr, nullptr);
-  return hip_result(replay(cfg, 1, a, as_stream(stream)), "flush");
+  return replay(cfg, 1, a, as_stream(stream), "flush");
 }
 
 int replayssm_flush_selected(const replayssm_config* cfg, const replayssm_state* st,
@@ -383,7 +392,7 @@ int replayssm_flush_selected(const replayssm_config* cfg, const replayssm_state*
   NEED(select);
   rs::ReplayArgs a = replay_args(cfg, st, 0, rs::kModeFlush, nullptr, nullptr);
   a.select = select;
-  return hip_result(replay(cfg, 1, a, as_stream(stream)), "flush_selected");
+  return replay(cfg, 1, a, as_stream(stream), "flush_selected");
 }
 
 int replayssm_snapshot(const replayssm_config* cfg, const replayssm_state* st, int n,

@@ -110,13 +110,17 @@ struct EagerArgs {
 // Dynamic LDS carve-up of the replay kernel, in floats. Every block starts on a
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
 // wavefront reading one column of four consecutive rows hit distinct banks;
-// windows too long for that within kMaxLdsBytes use unpadded rows instead.
+// windows too long for that within kLdsPaddedBudget use unpadded rows instead
+// (the padding would cost workgroups per compute unit). The carve may exceed
+// that budget up to what the device gives one workgroup (kArchMaxLdsBytes on
+// gfx950, 160 KiB per compute unit; each launch checks the device's own figure).
 // The kernel kind changes blocks: GDN with the two-precision checkpoint adds the
 // Gram matrix k_i . k_j of the staged records (its exact fold); KDA has a gate
 // row per record instead of a scalar, no decay-product tables, and adds the
 // drafts' queries and keys scaled by the gates since the last committed record,
 // and the committed records' column decay.
-constexpr int kMaxLdsBytes = 64 * 1024;
+constexpr int kLdsPaddedBudget = 64 * 1024;
+constexpr int kArchMaxLdsBytes = 160 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
   int k, v, alpha, beta, q, gq, gk, cq, ck, gram, qg, kg, pf, total;
@@ -124,7 +128,7 @@ struct ReplayLds {
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
   __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, int kind = REPLAYSSM_MAMBA2) {
     carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), kind);
-    if (total * 4 > kMaxLdsBytes) carve(C, dk, dv, tmax, dk, dv, kind);
+    if (total * 4 > kLdsPaddedBudget) carve(C, dk, dv, tmax, dk, dv, kind);
   }
   __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, int kind) {
     const bool with_gram = kind == kKindGdnExact, kda = kind == REPLAYSSM_KDA;
@@ -151,6 +155,9 @@ struct ReplayLds {
 // the current device at once (occupancy x compute units), at most `items`.
 // The occupancy of each (kernel, block, LDS) triple is computed once and cached.
 hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid);
+
+// Largest dynamic LDS one workgroup may use on the current device, in bytes (cached per device).
+hipError_t device_max_lds(int* bytes);
 
 // Launchers (one per kernel family); they return hipError_t of the launch.
 hipError_t launch_replay(int kind, int dk, int tmax, const ReplayArgs& a, hipStream_t s);

@@ -1075,9 +1075,24 @@ static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
   const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
   const int block = a.dv / (16 * RT) * kWave;
   const size_t smem = (size_t)lds.total * 4;
+  const void* fn = reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>);
+  hipError_t e;
+  if (smem > 64 * 1024) {
+    // long windows: the dynamic LDS a launch of this kernel may request is raised, once per
+    // device and size
+    static std::atomic<int> raised[64];
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (raised[dev].load(std::memory_order_acquire) < (int)smem) {
+      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      raised[dev].store((int)smem, std::memory_order_release);
+    }
+  }
   int grid = 0;
-  hipError_t e = persistent_grid(reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>), block,
-                                 smem, a.B * a.H, &grid);
+  e = persistent_grid(fn, block, smem, a.B * a.H, &grid);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED, RT>), dim3((unsigned)grid), dim3((unsigned)block), smem,
                      s, a);

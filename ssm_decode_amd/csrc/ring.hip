@@ -23,6 +23,26 @@ hipError_t device_cus(int* cus) {
   return hipSuccess;
 }
 
+hipError_t device_max_lds(int* bytes) {
+  static std::mutex mu;
+  static int lds[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (lds[dev] == 0) {
+    int per_block = 0, optin = 0;
+    e = hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    // (the opt-in figure, where the runtime reports one, is what a launch may request)
+    if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess) optin = 0;
+    lds[dev] = optin > per_block ? optin : per_block;
+  }
+  *bytes = lds[dev];
+  return hipSuccess;
+}
+
 hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid) {
   struct Entry {
     const void* kernel;

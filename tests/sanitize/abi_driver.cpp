@@ -21,6 +21,7 @@ static hipError_t count() {
 hipError_t persistent_grid(const void*, int, size_t, int, int* grid) { *grid = 1; return count(); }
 hipError_t launch_replay(int, int, int, const ReplayArgs&, hipStream_t) { return count(); }
 hipError_t launch_append(int, const AppendArgs&, hipStream_t) { return count(); }
+hipError_t device_max_lds(int* bytes) { *bytes = kArchMaxLdsBytes; return hipSuccess; }
 hipError_t launch_append_static(int, const AppendArgs& a, hipStream_t) { return a.arrive ? hipErrorInvalidValue : count(); }
 hipError_t launch_accept(int32_t*, int32_t*, int32_t*, const int32_t*, int, int, hipStream_t) { return count(); }
 hipError_t launch_init(int32_t*, int32_t*, int32_t*, int64_t*, int32_t*, int32_t*, int, hipStream_t) { return count(); }

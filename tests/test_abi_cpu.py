@@ -70,10 +70,10 @@ def test_sizes_of_the_b256_mamba2_layer(rs):
     assert s6.ring_vraw_bytes == 0 and s6.hp_bytes == 256 * 32 * 128 * 128 * 4
 
 
-@pytest.mark.parametrize("L,T", [(4, 1), (4, 4), (8, 8), (16, 8), (32, 8), (64, 1), (64, 4)])
+@pytest.mark.parametrize("L,T", [(4, 1), (4, 4), (8, 8), (16, 8), (32, 8), (64, 1), (64, 4), (64, 8)])
 def test_window_sweep_configs_fit(rs, L, T):
-    """Every window of the sweep fits the LDS budget at the real head shape (dv=64, dk=128),
-    except L=64 with T=8; L=64 with T=4 fits only with unpadded record rows."""
+    """Every window of the sweep fits a gfx950 workgroup's LDS at the real head shape (dv=64,
+    dk=128); from L=64 with T=4 on with unpadded record rows, L=64 with T=8 past 64 KiB."""
     cfg = rs.make_config("mamba2", "fp32", 256, 128, 64, 128, L, T)
     assert rs.get_sizes(cfg).C == L + T
 
@@ -83,10 +83,11 @@ def test_window_sweep_configs_fit(rs, L, T):
     (dict(dv=24), -1), (dict(dv=272), -1), (dict(dk=48), -1), (dict(dk=256), -1), (dict(L=0), -1),
     (dict(L=65), -1), (dict(T_max=0), -1), (dict(T_max=9, L=16), -1), (dict(T_max=5, L=4), -1),
     (dict(precision="fp32_hp_bf16_lp", dk=16, dv=16), -2), (dict(kind="gdn", precision="bf16_shared"), -2),
-    (dict(kind="gdn", precision="fp32_hp_bf16_lp", L=64, T_max=4, dv=128), -2),
-    (dict(L=64, T_max=8, dv=256, dk=128), -2), (dict(L=64, T_max=8), -2),
+    (dict(kind="gdn", precision="fp32_hp_bf16_lp", L=64, T_max=4, dv=128), 0),
+    (dict(L=64, T_max=8, dv=256, dk=128), 0), (dict(L=64, T_max=8), 0),
     (dict(kind="kda", precision="fp32_hp_bf16_lp"), -2), (dict(kind="kda", precision="bf16_shared"), -2),
-    (dict(kind="kda", L=64, T_max=8, dv=128), -2), (dict(kind="kda"), 0), (dict(kind="kda", dk=16, dv=16, L=64), 0),
+    (dict(kind="kda", L=64, T_max=8, dv=128), 0), (dict(kind="kda", L=64, T_max=8, dv=256), -2),
+    (dict(kind="kda"), 0), (dict(kind="kda", dk=16, dv=16, L=64), 0),
 ])
 def test_config_validation(rs, kw, code):
     base = dict(kind="mamba2", precision="fp32", B=2, H=3, dv=64, dk=128, L=16, T_max=4)
