@@ -318,6 +318,12 @@ __device__ __forceinline__ void store_records(const ReplayArgs& a, float* sm, co
   }
 }
 
+// Whether the mat-vecs run on the matrix cores (matvec_mfma in replay_item): the delta-rule
+// kinds with 4 or 8 drafts, whose 8 or 16 right-hand vectors fill half or all of the operand.
+// (Timed against the vector form on MI355X: equal within run-to-run spread for every kind.)
+template <int KIND, int TMAX>
+constexpr bool kMfmaMatvec = kind_gdn(KIND) && TMAX >= 4;
+
 // One item. On entry S holds (or is loading) the checkpoint copy the item's
 // route reads, and rr its ring rows; both were requested during the previous
 // item. On return rr holds (or is loading) the rows of `next` and S its
@@ -457,6 +463,48 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
             if (GDN) yk[tl][i] = fma4(S[tl * NT + nt], kv, yk[tl][i]);
           }
         }
+      }
+    }
+  };
+
+  // The same mat-vecs on the matrix cores, for the delta-rule kinds with 4 or 8 drafts, whose
+  // 2 T right-hand vectors q_1..T, k_1..T (KDA: the gated qg, kg) fill half or all of a 16-wide
+  // MFMA operand. Y^T = [Q | K]^T S^T is a sum of v_mfma_f32_16x16x4_f32 steps over the
+  // checkpoint registers, which are already the B operand: lane (g, col) holds
+  // S[row col][16 nt + 4 g + e], i.e. B[k = g][p = col] of step (nt, e), whose four columns are
+  // n = 16 nt + 4 k + e. Lane (g, col) supplies A[i = col][k = g], entry 16 nt + 4 g + e of
+  // vector i (q_i for i < TMAX, k_{i - TMAX} after; zero for absent drafts and past 2 TMAX),
+  // and receives D[4 g + r][col]: vector 4 g + r at its row, summed over every column. Lane
+  // group g = i / 4 thus holds vector i's whole sum and the other groups zero, so the group
+  // sums of the output phase leave it unchanged.
+  auto matvec_mfma = [&]() {
+    const int vi = col;
+    const bool isq = vi < TMAX;
+    const int d = isq ? vi : vi - TMAX;
+    const bool live = vi < 2 * TMAX && d < T;
+    const float* src = isq ? (KDA ? sm + lds.qg + d * DK : sm + lds.q + d * DK)
+                           : (KDA ? sm + lds.kg + d * DK : sm + lds.k + (hc + d) * lds.dks);
+    src = (live ? src : sm + lds.q) + 4 * g;
+    f32x4 acc[RT];
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 a4 = ld4(src + nt * 16);
+      if (!live) a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int tl = 0; tl < RT; ++tl)
+          acc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], S[tl * NT + nt][e], acc[tl], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl) {
+#pragma unroll
+      for (int i = 0; i < TMAX; ++i) {
+        const int vq = i, vk = TMAX + i;
+        yq[tl][i] = (g == (vq >> 2)) ? acc[tl][vq & 3] : 0.f;
+        yk[tl][i] = (g == (vk >> 2)) ? acc[tl][vk & 3] : 0.f;
       }
     }
   };
@@ -936,7 +984,11 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
     }
   }
   if (fold) fold_state();
-  if (outputs) matvec();
+  if constexpr (kMfmaMatvec<KIND, TMAX>) {
+    if (outputs) matvec_mfma();
+  } else {
+    if (outputs) matvec();
+  }
   prefetch_next();
   scans_and_dots();
   __syncthreads();
