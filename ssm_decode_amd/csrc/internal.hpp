@@ -115,7 +115,7 @@ struct EagerArgs {
 // that budget up to what the device gives one workgroup (kArchMaxLdsBytes on
 // gfx950, 160 KiB per compute unit; each launch checks the device's own figure).
 // The kernel kind changes blocks: GDN with the two-precision checkpoint adds the
-// Gram matrix k_i . k_j of the staged records (its exact fold); KDA has a gate
+// Gram blocks k_i . k_j of the staged records and a table of S k_j (its exact fold); KDA has a gate
 // row per record instead of a scalar, no decay-product tables, and adds the
 // drafts' queries and keys scaled by the gates since the last committed record,
 // and the committed records' column decay.
@@ -123,7 +123,7 @@ constexpr int kLdsPaddedBudget = 64 * 1024;
 constexpr int kArchMaxLdsBytes = 160 * 1024;
 struct ReplayLds {
   int dks, dvs;  // row strides of the k and v record rows
-  int k, v, alpha, beta, q, gq, gk, cq, ck, gram, qg, kg, pf, total;
+  int k, v, alpha, beta, q, gq, gk, cq, ck, gram, ytab, ys, qg, kg, pf, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
   __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, int kind = REPLAYSSM_MAMBA2) {
@@ -144,7 +144,11 @@ struct ReplayLds {
     cq = gk + (kda ? 0 : pad4((C + 1) * tmax));
     ck = cq + pad4(C * tmax);
     gram = ck + pad4(C * tmax);
-    qg = gram + (with_gram ? pad4(C * C) : 0);
+    // (exact-correction fold: the Gram matrix's diagonal 16 x 16 blocks, and S k_j of one
+    // block of 16 records for every state row, row stride dv + 4)
+    ytab = gram + (with_gram ? ((C + 15) / 16) * 256 : 0);
+    ys = dv + 4;
+    qg = ytab + (with_gram ? 16 * ys : 0);
     kg = qg + (kda ? tmax * dk : 0);
     pf = kg + (kda ? tmax * dk : 0);
     total = pf + (kda ? dk : 0);

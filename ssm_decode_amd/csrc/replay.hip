@@ -626,18 +626,22 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
   // record was computed from the bf16 copy ("How it works": Gated DeltaNet and
   // Two precisions). Such a fold instead recomputes every correction from the
   // fp32 checkpoint it follows (the staged v rows hold the raw v here), so the
-  // bf16 rounding never reaches S. Records go in blocks of four: with S the state
+  // bf16 rounding never reaches S. Records go in blocks of 16. With S the state
   // before the block, D_j the decay from the block start to just before record j
   // and g_ij = prod of alpha over (i, j),
   //   w_j = D_j S k_j + sum_{i<j in block} g_ij (k_i . k_j) u_i,  u_j = beta_j (v_j - alpha_j w_j),
-  // then S <- D S + sum_i g_i u_i k_i^T over the block (D and g_i to its end) as one
-  // MFMA rank-4 step per tile. The four mat-vecs of a block are independent.
+  // then S <- D S + sum_i g_i u_i k_i^T over the block (D and g_i to its end). The block's
+  // mat-vecs S k_j are one MFMA pass (the 16 keys fill the right-hand operand, as in
+  // matvec_mfma), the corrections are solved row by row (a lane per state row, records in
+  // order), and the update is one MFMA rank-16 step per tile.
+  constexpr int kEB = 8;  // records per block (a divisor of 16: blocks never straddle a Gram block)
   auto exact_fold_state = [&]() {
-    // Gram matrix of the staged committed keys, diagonal 16 x 16 blocks (the only
-    // pairs a block of four needs), by every wavefront (identical values): lane l
-    // supplies A[l & 15][l >> 4] = k_{16 jb + (l & 15)}[n] and B[l >> 4][l & 15] =
-    // k_{16 jb + (l & 15)}[n] for n = 16 c + 4 (l >> 4) + e; the result gives lane l
-    // entry (16 jb + 4 (l >> 4) + r, 16 jb + (l & 15)), r = 0..3.
+    // Coefficients c_im = g_im (k_i . k_m) of the records' mutual terms, i < m in one block of
+    // 16 (the diagonal blocks of the Gram matrix, scaled by the decays between the two
+    // records), by every wavefront (identical values): lane l supplies
+    // A[l & 15][l >> 4] = k_{16 jb + (l & 15)}[n] and B[l >> 4][l & 15] = k_{16 jb + (l & 15)}[n]
+    // for n = 16 c + 4 (l >> 4) + e; the result gives lane l the product of keys
+    // i = l & 15 and m = 4 (l >> 4) + r of block jb, r = 0..3, stored at (i, m).
     for (int jb = 0; 16 * jb < hc; ++jb) {
       const int ja = 16 * jb + col;
       const float* krow = sm + lds.k + (ja < hc ? ja : 0) * lds.dks + 4 * g;
@@ -648,76 +652,96 @@ __device__ __forceinline__ void replay_item(const ReplayArgs& a, float* sm, cons
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[e], f[e], acc, 0, 0, 0);
       }
+      // g_im = prod of alpha over (i, m), walked up from i = col; zero unless i < m
+      float gv[4] = {0.f, 0.f, 0.f, 0.f};
+      float prod = 1.f;
+      for (int m = 0; m < 16; ++m) {
+        const float am = sm[lds.alpha + 16 * jb + m];
+        if (m > col) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jb + 4 * g + r;
-        if (j < hc && ja < hc) sm[lds.gram + ja * C + j] = acc[r];
+          for (int r = 0; r < 4; ++r)
+            if (m == 4 * g + r) gv[r] = prod;
+          prod *= am;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm[lds.gram + jb * 256 + col * 16 + 4 * g + r] = gv[r] * acc[r];
     }
-    for (int j0 = 0; j0 < hc; j0 += 4) {
-      const int nb = hc - j0 < 4 ? hc - j0 : 4;
-      float w0[RT][4];
+    __builtin_amdgcn_wave_barrier();
+    for (int j0 = 0; j0 < hc; j0 += kEB) {
+      const int nb = hc - j0 < kEB ? hc - j0 : kEB;
+      const float* gblk = sm + lds.gram + (j0 >> 4) * 256 + (j0 & 15) * 17;
+      // S k_j for the block's records, every row of the wavefront's tiles: lane (g, col)
+      // supplies entry 16 nt + 4 g + e of key j0 + col and receives keys 4 g + r at row col
+      {
+        const bool live = col < nb;  // (keys past the block: zero)
+        const float* src = sm + lds.k + (live ? j0 + col : 0) * lds.dks + 4 * g;
+        f32x4 acc[RT];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float* kj = sm + lds.k + (jj < nb ? j0 + jj : 0) * lds.dks + 4 * g;
-        float part[RT];
-#pragma unroll
-        for (int tl = 0; tl < RT; ++tl) part[tl] = 0.f;
+        for (int tl = 0; tl < RT; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const f32x4 kv = ld4(kj + 16 * nt);
+          f32x4 a4 = ld4(src + nt * 16);
+          if (!live) a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int tl = 0; tl < RT; ++tl) part[tl] = fma4(S[tl * NT + nt], kv, part[tl]);
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int tl = 0; tl < RT; ++tl)
+              acc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], S[tl * NT + nt][e], acc[tl], 0, 0, 0);
         }
 #pragma unroll
-        for (int tl = 0; tl < RT; ++tl) w0[tl][jj] = part[tl];
+        for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm[lds.ytab + (4 * g + r) * lds.ys + prow + 16 * tl] = acc[tl][r];
       }
+      __builtin_amdgcn_wave_barrier();
+      // the corrections, a lane per state row of the wavefront (its RT tiles' 16 RT rows), the
+      // records in order; u_j replaces the staged raw v_j (no longer needed)
+      if (lane < 16 * RT) {
+        const int row = wave * RT * 16 + lane;
+        float wp[kEB];
 #pragma unroll
-      for (int tl = 0; tl < RT; ++tl)
+        for (int m = 0; m < kEB; ++m) wp[m] = 0.f;
+        float Dm = 1.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w0[tl][jj] = sum_groups(w0[tl][jj]);
-      float u[RT][4];
-      float D = 1.f;
+        for (int m = 0; m < kEB; ++m) {
+          if (m < nb) {
+            const int j = j0 + m;
+            const float al = sm[lds.alpha + j];
+            const float w = Dm * sm[lds.ytab + m * lds.ys + row] + wp[m];
+            const float u = sm[lds.beta + j] * (sm[lds.v + j * lds.dvs + row] - al * w);
+            sm[lds.v + j * lds.dvs + row] = u;
+            // its term in the corrections of the block's later records: row m of the coefficients
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-        for (int tl = 0; tl < RT; ++tl) u[tl][jj] = 0.f;
-        if (jj < nb) {
-          const int j = j0 + jj;
-          const float al = sm[lds.alpha + j];
-          const float be = sm[lds.beta + j];
-#pragma unroll
-          for (int tl = 0; tl < RT; ++tl) {
-            float w = D * w0[tl][jj];
-            float gij = 1.f;
-#pragma unroll
-            for (int ii = jj - 1; ii >= 0; --ii) {
-              w += gij * sm[lds.gram + (j0 + ii) * C + j] * u[tl][ii];
-              gij *= sm[lds.alpha + j0 + ii];
-            }
-            u[tl][jj] = be * (sm[lds.v + j * lds.dvs + prow + 16 * tl] - al * w);
+            for (int m2 = m + 1; m2 < kEB; ++m2) wp[m2] = __builtin_fmaf(gblk[m * 16 + m2], u, wp[m2]);
+            Dm *= al;
           }
-          D *= al;
         }
       }
-      // decay of record j0 + g from itself to the end of the block
-      float ge = 1.f;
-      for (int m = j0 + g + 1; m < j0 + nb; ++m) ge *= sm[lds.alpha + m];
-      const bool vj = g < nb;
-      float bval[RT];
+      __builtin_amdgcn_wave_barrier();
+      // S <- D S + sum_m gamma_m u_m k_m^T: lane t of the scan holds the block's alpha_{j0 + t}
+      const float sp = suffix_product64(lane < nb ? sm[lds.alpha + j0 + lane] : 1.f, lane);
+      const float D = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sp), 0));
 #pragma unroll
-      for (int tl = 0; tl < RT; ++tl)
-        bval[tl] = vj ? ge * (g == 0 ? u[tl][0] : g == 1 ? u[tl][1] : g == 2 ? u[tl][2] : u[tl][3]) : 0.f;
-      const float* krow = sm + lds.k + (vj ? j0 + g : 0) * lds.dks + col;
+      for (int nt = 0; nt < RT * NT; ++nt) S[nt] *= D;
+      for (int kc = 0; 4 * kc < nb; ++kc) {
+        const int m = 4 * kc + g;
+        const bool vj = m < nb;
+        const float wm = __shfl(sp, m + 1, kWave);  // prod of alpha over (m, nb): lanes past nb hold 1
+        float bval[RT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float aval = vj ? krow[nt * 16] : 0.f;
+        for (int tl = 0; tl < RT; ++tl)
+          bval[tl] = vj ? wm * sm[lds.v + (j0 + m) * lds.dvs + prow + 16 * tl] : 0.f;
+        const float* krow = sm + lds.k + (vj ? j0 + m : 0) * lds.dks + col;
 #pragma unroll
-        for (int tl = 0; tl < RT; ++tl) {
-          S[tl * NT + nt] *= D;
-          S[tl * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval[tl], S[tl * NT + nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const float aval = vj ? krow[nt * 16] : 0.f;
+#pragma unroll
+          for (int tl = 0; tl < RT; ++tl)
+            S[tl * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aval, bval[tl], S[tl * NT + nt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_wave_barrier();
     }
   };
 
