@@ -95,6 +95,7 @@ def parse():
     ap.add_argument("--workload", default="mamba2_decode_b256")
     ap.add_argument("--quick", action="store_true", help="headline workload only (no extras, no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-drift", action="store_true", help="skip the drift leg (1024-round comparisons)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="cap on the timed oracle seconds of each CPU-baseline figure")
     ap.add_argument("--sweep", action="store_true", help="also run the batch sweep of the two-precision layer")
@@ -926,7 +927,9 @@ def main():
                         "verify_kernel_gbs": r["kernel_gbs"], "verify_avg_us": r["kernel_avg_us"]}
         r4["small_batch_graph"] = {f"B{B}": run_spec_graph(torch, rs, synth, w4, B, 16, 20, args.seed)
                                    for B in (1, 32)}
-        line["drift"] = {f"B{B}": run_drift(torch, rs, synth, w4, B, w4.steps, args.seed) for B in (256, 1, 32, 512)}
+        if not args.no_drift:
+            line["drift"] = {f"B{B}": run_drift(torch, rs, synth, w4, B, w4.steps, args.seed)
+                             for B in (256, 1, 32, 512)}
         if args.sweep:
             sweep = {}
             for B in (1, 32, 256, 512):
