@@ -416,8 +416,9 @@ int replayssm_conv_accept(const replayssm_conv_config* cfg, const replayssm_conv
  * 64 (dv < 128), 6 (dv >= 128) or 3 (dv >= 128, Gated DeltaNet with the two-precision
  * checkpoint) (sequence, head) items per compute unit of the current device, where their
  * throughput was measured higher, and one tile for smaller batches, whose latency one tile
- * keeps lower. Process-wide; takes effect at the next launch. EINVAL for
- * another value. */
+ * keeps lower; and only where two tiles fit more workgroups on a compute unit than one (long
+ * windows, whose record staging in LDS holds both to the same count, take one tile).
+ * Process-wide; takes effect at the next launch. EINVAL for another value. */
 #define REPLAYSSM_TILES_AUTO 0
 #define REPLAYSSM_TILES_ONE 1
 #define REPLAYSSM_TILES_TWO 2

@@ -37,7 +37,9 @@ bool exact_u(const replayssm_config* c);
 // Launches the replay kernel after checking its LDS carve against what the current device
 // gives one workgroup (ENOTSUP beyond it).
 int replay(const replayssm_config* cfg, int tmax, const rs::ReplayArgs& a, hipStream_t s, const char* what) {
-  const rs::ReplayLds lds(cfg->L + cfg->T_max, cfg->dk, cfg->dv, tmax, exact_u(cfg) ? rs::kKindGdnExact : cfg->kind);
+  // (the launcher may pick padded rows where they fit more workgroups; the unpadded carve is the least LDS)
+  const rs::ReplayLds lds(cfg->L + cfg->T_max, cfg->dk, cfg->dv, tmax, exact_u(cfg) ? rs::kKindGdnExact : cfg->kind,
+                          true);
   int max_lds = 0;
   if (int r = hip_result(rs::device_max_lds(&max_lds), what)) return r;
   if (lds.total * 4 > max_lds)
@@ -92,7 +94,7 @@ int check_config(const replayssm_config* c) {
                 "the shared bf16 checkpoint is built for Mamba-2 only (GDN takes FP32 or "
                 "FP32_HP_BF16_LP)");
   const rs::ReplayLds lds(c->L + c->T_max, c->dk, c->dv, tmax_bucket(c->T_max),
-                          exact_u(c) ? rs::kKindGdnExact : c->kind);
+                          exact_u(c) ? rs::kKindGdnExact : c->kind, true);
   if (lds.total * 4 > rs::kArchMaxLdsBytes)
     return fail(REPLAYSSM_ENOTSUP, "L + T_max and dims need %d bytes of LDS (> %d on gfx950)", lds.total * 4,
                 rs::kArchMaxLdsBytes);

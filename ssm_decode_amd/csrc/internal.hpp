@@ -66,6 +66,7 @@ struct ReplayArgs {
   const float* in_k;      // [B][T][H][dk]
   const float* in_v;      // [B][T][H][dv]
   int fused;
+  int lds_unpadded;  // set by the launcher: the LDS carve uses unpadded record rows
   int B, H, dv, L, C, T;
   int precision;
   int mode;
@@ -109,9 +110,10 @@ struct EagerArgs {
 
 // Dynamic LDS carve-up of the replay kernel, in floats. Every block starts on a
 // 16-byte boundary. Row strides are padded so that the four 16-lane groups of a
-// wavefront reading one column of four consecutive rows hit distinct banks;
-// windows too long for that within kLdsPaddedBudget use unpadded rows instead
-// (the padding would cost workgroups per compute unit). The carve may exceed
+// wavefront reading one column of four consecutive rows hit distinct banks,
+// unless the launcher asks for unpadded rows (when they let more workgroups
+// share a compute unit: long windows, whose padded carve is what limits the
+// occupancy) or the padded carve passes kLdsPaddedBudget. The carve may exceed
 // that budget up to what the device gives one workgroup (kArchMaxLdsBytes on
 // gfx950, 160 KiB per compute unit; each launch checks the device's own figure).
 // The kernel kind changes blocks: GDN with the two-precision checkpoint adds the
@@ -126,9 +128,10 @@ struct ReplayLds {
   int k, v, alpha, beta, q, gq, gk, cq, ck, gram, ytab, ys, qg, kg, pf, total;
   __host__ __device__ static int pad4(int x) { return (x + 3) & ~3; }
   __host__ __device__ static int row_stride(int d) { return ((d / 16) & 1) ? d : d + 16; }
-  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, int kind = REPLAYSSM_MAMBA2) {
+  __host__ __device__ ReplayLds(int C, int dk, int dv, int tmax, int kind = REPLAYSSM_MAMBA2,
+                                bool unpadded = false) {
     carve(C, dk, dv, tmax, row_stride(dk), row_stride(dv), kind);
-    if (total * 4 > kLdsPaddedBudget) carve(C, dk, dv, tmax, dk, dv, kind);
+    if (unpadded || total * 4 > kLdsPaddedBudget) carve(C, dk, dv, tmax, dk, dv, kind);
   }
   __host__ __device__ void carve(int C, int dk, int dv, int tmax, int kstride, int vstride, int kind) {
     const bool with_gram = kind == kKindGdnExact, kda = kind == REPLAYSSM_KDA;
@@ -159,6 +162,8 @@ struct ReplayLds {
 // the current device at once (occupancy x compute units), at most `items`.
 // The occupancy of each (kernel, block, LDS) triple is computed once and cached.
 hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid);
+// Workgroups of `kernel` that can be resident on one compute unit of the current device (cached).
+hipError_t blocks_per_cu(const void* kernel, int block, size_t smem, int* per_cu);
 
 // Largest dynamic LDS one workgroup may use on the current device, in bytes (cached per device).
 hipError_t device_max_lds(int* bytes);

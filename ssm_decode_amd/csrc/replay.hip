@@ -46,6 +46,9 @@
 // records without waiting for its checkpoint, and for its checkpoint without
 // waiting for the records requested after it.
 #include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "route.hpp"
 
@@ -1100,7 +1103,7 @@ __global__ void __launch_bounds__(1024 / RT) replay_kernel(const ReplayArgs a) {
   RecRegs<TMAX, RT> rr;
   // Loop invariants of the workgroup: the LDS carve-up and where a thread's
   // share of the ring rows lies.
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
+  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND, a.lds_unpadded != 0);
   const StageMap map(threadIdx.x, blockDim.x, NT * 4, a.dv);
   // Items advance by the grid size G: (sequence, head) advances by (G / H, G % H)
   // with a carry, so no item divides by H.
@@ -1146,32 +1149,71 @@ __global__ void __launch_bounds__(1024 / RT) replay_kernel(const ReplayArgs a) {
   if (flag[0]) commit_pointers(a, threadIdx.x, blockDim.x);
 }
 
-template <int KIND, int NT, int TMAX, bool FUSED, int RT>
-static hipError_t launch_t(const ReplayArgs& a, hipStream_t s) {
-  const ReplayLds lds(a.C, NT * 16, a.dv, TMAX, KIND);
-  const int block = a.dv / (16 * RT) * kWave;
-  const size_t smem = (size_t)lds.total * 4;
-  const void* fn = reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>);
-  hipError_t e;
-  if (smem > 64 * 1024) {
-    // long windows: the dynamic LDS a launch of this kernel may request is raised, once per
-    // device and size
-    static std::atomic<int> raised[64];
-    int dev = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (raised[dev].load(std::memory_order_acquire) < (int)smem) {
-      e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      if (e != hipSuccess) return e;
-      raised[dev].store((int)smem, std::memory_order_release);
-    }
-  }
-  int grid = 0;
-  e = persistent_grid(fn, block, smem, a.B * a.H, &grid);
+// How one instantiation runs a call: its dynamic LDS (record rows padded or not) and the
+// workgroups of it that fit on a compute unit. Padded rows (no bank conflicts) unless unpadded
+// ones let more workgroups share a compute unit where the padded carve leaves fewer than four
+// (long windows, whose staging then sets the occupancy). Measured at B=256, Mamba-2 64x128:
+// L=64, T=1 two -> three workgroups, 3.72 -> 4.76 TB/s; L=32, T=8 three -> four, +8 %; but
+// L=32, T=4 four -> five ran 20 % slower (the bank conflicts of unpadded rows cost more than
+// the fifth workgroup).
+struct LaunchPlan {
+  int unpadded;
+  size_t smem;
+  int per_cu;
+};
+
+// Raises the dynamic LDS a launch of `fn` may request (beyond 64 KiB), once per device and size.
+static hipError_t allow_lds(const void* fn, size_t smem) {
+  if (smem <= 64 * 1024) return hipSuccess;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> raised[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED, RT>), dim3((unsigned)grid), dim3((unsigned)block), smem,
-                     s, a);
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& x : raised[dev])
+    if (x.first == fn && x.second >= (int)smem) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  raised[dev].push_back({fn, (int)smem});
+  return hipSuccess;
+}
+
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
+static hipError_t plan_t(const ReplayArgs& a, LaunchPlan* plan) {
+  const int block = a.dv / (16 * RT) * kWave;
+  const void* fn = reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>);
+  const ReplayLds padded(a.C, NT * 16, a.dv, TMAX, KIND, false), unpadded(a.C, NT * 16, a.dv, TMAX, KIND, true);
+  hipError_t e = allow_lds(fn, (size_t)padded.total * 4);
+  if (e != hipSuccess) return e;
+  int occ_p = 0;
+  e = blocks_per_cu(fn, block, (size_t)padded.total * 4, &occ_p);
+  if (e != hipSuccess) return e;
+  *plan = LaunchPlan{0, (size_t)padded.total * 4, occ_p};
+  if (unpadded.total < padded.total && occ_p < 4) {
+    int occ_u = 0;
+    e = blocks_per_cu(fn, block, (size_t)unpadded.total * 4, &occ_u);
+    if (e != hipSuccess) return e;
+    if (occ_u > occ_p) *plan = LaunchPlan{1, (size_t)unpadded.total * 4, occ_u};
+  }
+  return hipSuccess;
+}
+
+template <int KIND, int NT, int TMAX, bool FUSED, int RT>
+static hipError_t launch_t(const ReplayArgs& args, hipStream_t s) {
+  const int block = args.dv / (16 * RT) * kWave;
+  const void* fn = reinterpret_cast<const void*>(&replay_kernel<KIND, NT, TMAX, FUSED, RT>);
+  LaunchPlan plan;
+  hipError_t e = plan_t<KIND, NT, TMAX, FUSED, RT>(args, &plan);
+  if (e != hipSuccess) return e;
+  ReplayArgs a = args;
+  a.lds_unpadded = plan.unpadded;
+  int grid = 0;
+  e = persistent_grid(fn, block, plan.smem, a.B * a.H, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((replay_kernel<KIND, NT, TMAX, FUSED, RT>), dim3((unsigned)grid), dim3((unsigned)block),
+                     plan.smem, s, a);
   return hipGetLastError();
 }
 
@@ -1216,12 +1258,32 @@ static hipError_t launch_r(const ReplayArgs& a, hipStream_t s) {
   return a.fused ? launch_t<KIND, NT, TMAX, true, RT>(a, s) : launch_t<KIND, NT, TMAX, false, RT>(a, s);
 }
 
+// Two tiles also need to put more items in flight than one: where the record staging's LDS
+// holds both forms to the same workgroups per compute unit (long windows), one tile's twice as
+// many wavefronts finish each item sooner. Measured at B=256, Mamba-2 64x128, one against two
+// tiles: L=64, T=1 0.71 against 0.61 M tokens/s; L=64, T=4 0.86 against 0.62 M accepted
+// tokens/s; L=32, T=4 1.31 against 1.25 M; L=16 within 0.5 %.
+template <int KIND, int NT, int TMAX>
+static hipError_t more_in_flight_with_two(const ReplayArgs& a, bool* two) {
+  LaunchPlan p1, p2;
+  hipError_t e = a.fused ? plan_t<KIND, NT, TMAX, true, 1>(a, &p1) : plan_t<KIND, NT, TMAX, false, 1>(a, &p1);
+  if (e != hipSuccess) return e;
+  e = a.fused ? plan_t<KIND, NT, TMAX, true, 2>(a, &p2) : plan_t<KIND, NT, TMAX, false, 2>(a, &p2);
+  if (e != hipSuccess) return e;
+  *two = p2.per_cu > p1.per_cu;
+  return hipSuccess;
+}
+
 template <int KIND, int NT, int TMAX>
 static hipError_t launch_f(const ReplayArgs& a, hipStream_t s) {
   if constexpr (kTwoTiles<KIND, NT, TMAX>) {
     bool two = false;
     hipError_t e = two_tiles(a, KIND == kKindGdnExact, &two);
     if (e != hipSuccess) return e;
+    if (two && get_tiling() == REPLAYSSM_TILES_AUTO) {
+      e = more_in_flight_with_two<KIND, NT, TMAX>(a, &two);
+      if (e != hipSuccess) return e;
+    }
     if (two) return launch_r<KIND, NT, TMAX, 2>(a, s);
   }
   return launch_r<KIND, NT, TMAX, 1>(a, s);

@@ -44,6 +44,18 @@ hipError_t device_max_lds(int* bytes) {
 }
 
 hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items, int* grid) {
+  int per_cu = 0, cus = 0;
+  hipError_t e = blocks_per_cu(kernel, block, smem, &per_cu);
+  if (e != hipSuccess) return e;
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const long g = (long)cus * per_cu;
+  *grid = (int)(g < items ? g : items);
+  if (*grid < 1) *grid = 1;
+  return hipSuccess;
+}
+
+hipError_t blocks_per_cu(const void* kernel, int block, size_t smem, int* per_cu_out) {
   struct Entry {
     const void* kernel;
     int block;
@@ -53,30 +65,21 @@ hipError_t persistent_grid(const void* kernel, int block, size_t smem, int items
   };
   static std::mutex mu;
   static std::vector<Entry> cache;
-  static int cus[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   int per_cu = -1;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (cus[dev] == 0) {
-      e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-    }
-    for (const Entry& x : cache)
-      if (x.kernel == kernel && x.block == block && x.smem == smem && x.device == dev) per_cu = x.per_cu;
-    if (per_cu < 0) {
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, smem);
-      if (e != hipSuccess) return e;
-      if (per_cu < 1) per_cu = 1;
-      cache.push_back(Entry{kernel, block, smem, dev, per_cu});
-    }
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& x : cache)
+    if (x.kernel == kernel && x.block == block && x.smem == smem && x.device == dev) per_cu = x.per_cu;
+  if (per_cu < 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, smem);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) per_cu = 1;
+    cache.push_back(Entry{kernel, block, smem, dev, per_cu});
   }
-  const long g = (long)cus[dev] * per_cu;
-  *grid = (int)(g < items ? g : items);
-  if (*grid < 1) *grid = 1;
+  *per_cu_out = per_cu;
   return hipSuccess;
 }
 
