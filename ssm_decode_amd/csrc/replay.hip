@@ -1066,6 +1066,27 @@ __device__ __forceinline__ void commit_pointers(const ReplayArgs& a, int tid, in
 
 // (dv <= 256: a workgroup is at most 1024 / RT threads, which also bounds the
 // registers the compiler may give a thread)
+// Wave priority by progress. A compute unit issues from its oldest waves first, so of the
+// workgroups sharing it the ones dispatched first get through their equal shares of items
+// sooner (measured: a Mamba-2 decode launch's first-dispatched workgroups end about 20 % before
+// the last-dispatched ones), and the launch waits for the slowest. Each workgroup lowers its
+// waves' priority by one step per quarter of its share: one that is ahead yields the issue slots
+// to those behind it. Measured at B = 256 against no priority change: GDN and KDA decode -3 to
+// -4 %, verify T = 4 -1.6 to -3 % (all kinds); Mamba-2 decode unchanged with the fp32
+// checkpoint and 1.4 % slower with the bf16 copy, so its one-draft kernels keep one priority.
+template <int KIND, int TMAX>
+constexpr bool kLevelled = !(KIND == REPLAYSSM_MAMBA2 && TMAX == 1);
+
+__device__ __forceinline__ void level_priority(int done, int share) {
+  int lvl = 3 - (4 * done) / share;
+  lvl = __builtin_amdgcn_readfirstlane(lvl < 0 ? 0 : lvl);
+  // (the priority is an immediate operand)
+  if (lvl == 3) __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int KIND, int NT, int TMAX, bool FUSED, int RT>
 __global__ void __launch_bounds__(1024 / RT) replay_kernel(const ReplayArgs a) {
   extern __shared__ f32x4 smem_v4[];
@@ -1127,6 +1148,7 @@ __global__ void __launch_bounds__(1024 / RT) replay_kernel(const ReplayArgs a) {
                         *reinterpret_cast<Tile*>(&S[tl * NT]));
   }
   for (int k = 0; it.id < items; ++k) {
+    if constexpr (kLevelled<KIND, TMAX>) level_priority(k, (items + G - 1) / G);
     const Item nit = advance(it);
     const int kn = (k + 1) & 63;
     if (kn == 0 && nit.id < items) batch(nit.id);
