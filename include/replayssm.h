@@ -33,8 +33,10 @@
  *  - The library keeps no per-layer state: calls on distinct states may run
  *    concurrently; calls on one state must be stream-ordered. Its only
  *    process-wide state is the kernel tiling policy (replayssm_set_tiling,
- *    shared by every thread and device; it never changes results) and the
- *    per-device caches of compute-unit counts and kernel occupancies.
+ *    shared by every thread and device; it never changes results), the
+ *    per-device caches of compute-unit counts and kernel occupancies, and the
+ *    per-device counter array of replayssm_append_static (whose calls on one
+ *    GPU must not overlap).
  *
  * Shapes use B sequences, H heads, dv = value/head dim (Mamba-2 P, GDN d_v),
  * dk = key/state dim (Mamba-2 N, GDN d_k), ring capacity C = L + T_max.
